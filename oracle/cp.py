@@ -164,7 +164,11 @@ def merge_outputs(partials, rows_total):
     o = np.zeros((b, rows_total, hq, d))
     for o_i, lse_i, row0 in partials:
         rows = lse_i.shape[2]
-        w = np.exp(lse_i - lse[:, :, row0:row0 + rows])      # [b, hq, rows]
+        # a partial with no visible key (L_i = -inf) is an empty sum: weight 0,
+        # also on rows where every partial is empty (then O = 0, L = -inf)
+        with np.errstate(invalid="ignore"):
+            w = np.where(np.isneginf(lse_i), 0.0,
+                         np.exp(lse_i - lse[:, :, row0:row0 + rows]))   # [b, hq, rows]
         o[:, row0:row0 + rows] += np.transpose(w, (0, 2, 1))[..., None] * o_i
     return o, lse
 

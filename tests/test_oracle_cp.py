@@ -190,6 +190,19 @@ def test_merge_empty_partial_is_identity():
     assert np.array_equal(o, o1) and np.array_equal(lse, l1)
 
 
+def test_merge_of_empty_partials_is_empty_sum():
+    """Rows whose partials all see no key merge to the core's own empty
+    result (attention over zero keys: O = 0, L = -inf)."""
+    rng = np.random.default_rng(4)
+    q, k, v = rng.standard_normal((1, 3, 2, 4)), rng.standard_normal((1, 5, 1, 4)), \
+        rng.standard_normal((1, 5, 1, 4))
+    e1 = attention_rows(q, k, v, [0, 0, 0])
+    e2 = attention_rows(q, k[:, :2], v[:, :2], [0, 0, 0])
+    o, lse = ocp.merge_outputs([(e1[0], e1[1], 0), (e2[0], e2[1], 0)], 3)
+    assert np.array_equal(o, e1[0]) and np.array_equal(lse, e1[1])
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
 def test_merge_equal_lse_averages():
     rng = np.random.default_rng(1)
     oa, ob = rng.standard_normal((1, 2, 1, 4)), rng.standard_normal((1, 2, 1, 4))

@@ -1,0 +1,190 @@
+"""Throughput of one GPU's context-parallel causal attention share.
+
+A step is one pass of the whole path over one batch of synthetic input
+already resident in HBM: the zigzag split of Q, K and V (three
+cpattn_partition launches), the cp blockwise-attention steps of the
+measured rank (cpattn_step_fwd; at step i the rank reads the K/V block of
+rank (rank - i) mod cp) and the LSE merge (cpattn_merge).  W untimed
+warm-up steps, then K timed steps bracketed by synchronisation.
+
+value = causal-effective FLOPs of the rank's share (4*d per visible query/
+key pair) / the measured time of a step.  Per-kernel times come from HIP
+events recorded on the stream the kernels run on.
+
+The CPU baseline times the fp64 oracle on the host cores on a bounded
+sample of the same rank share (every k-th local row, all heads).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-sample-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline (0 disables it)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, rank, target_s):
+    """Oracle (fp64, OpenMP) on every stride-th local row of the rank share."""
+    import numpy as np
+    from long_context_causal_amd.inputs import as_f32
+    from oracle import attention_rows, max_threads
+    from oracle import cp as ocp
+
+    pos_all = ocp.zigzag_positions(w.s, w.cp, rank)
+    per_row = 4 * w.d * w.hq * w.b * (pos_all + 1)      # FLOPs of each local row
+    # calibrate the rate on a few rows, then size the sample to ~target_s
+    def run(pos):
+        qf = as_f32(q[:, pos]).astype(np.float64)
+        hi = int(pos.max()) + 1
+        kf = as_f32(k[:, :hi]).astype(np.float64)
+        vf = as_f32(v[:, :hi]).astype(np.float64)
+        if w.rope_theta is not None:
+            qf = ocp.rope(qf, pos, w.rope_theta)
+            kf = ocp.rope(kf, np.arange(hi), w.rope_theta)
+        t0 = time.perf_counter()
+        attention_rows(qf, kf, vf, pos + 1)
+        return time.perf_counter() - t0
+    probe = pos_all[:: max(1, len(pos_all) // 16)]
+    t_probe = run(probe)
+    rate = (4 * w.d * w.hq * w.b * (probe + 1)).sum() / max(t_probe, 1e-6)
+    stride = max(1, int(np.ceil(per_row.sum() / rate / target_s)))
+    sample = pos_all[::stride]
+    dt = run(sample)
+    flops = float((4 * w.d * w.hq * w.b * (sample + 1)).sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": max_threads(),
+            "kind": "oracle",
+            "sample": f"rank {rank}: every {stride}th of its {len(pos_all)} local rows "
+                      f"({len(sample)} rows x {w.hq} heads x b={w.b}, all visible keys), "
+                      f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(collectives are out of scope); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from long_context_causal_amd import cpattn as C
+    from long_context_causal_amd.inputs import HEADLINE, WORKLOADS, make_inputs
+    from long_context_causal_amd.runner import CPProblem
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    rank = w.rank
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v)
+    buf = P.alloc_rank(rank, C.CPATTN_F32)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def one_step(evs=None):
+        def mark(tag):
+            if evs is not None:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                evs.append((tag, e))
+        mark("start")
+        P.partition(stream)
+        mark("partition")
+        for i in range(w.cp):
+            P.step(buf, i, stream)
+            mark(f"step{i}")
+        P.merge(buf, stream)
+        mark("merge")
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            one_step()
+        torch.cuda.synchronize()
+        all_evs = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            evs = []
+            one_step(evs)
+            all_evs.append(evs)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+    # per-kernel times (ms) from the events, averaged over the timed steps
+    part_ms, merge_ms, step_ms, total_ms = [], [], [[] for _ in range(w.cp)], []
+    for evs in all_evs:
+        d = dict(evs)
+        names = [t for t, _ in evs]
+        part_ms.append(d["start"].elapsed_time(d["partition"]))
+        prev = "partition"
+        for i in range(w.cp):
+            step_ms[i].append(d[prev].elapsed_time(d[f"step{i}"]))
+            prev = f"step{i}"
+        merge_ms.append(d[prev].elapsed_time(d["merge"]))
+        total_ms.append(d["start"].elapsed_time(d[names[-1]]))
+    mean = lambda xs: float(np.mean(xs))
+    ms_step = mean(total_ms)
+    steps_ms = [mean(x) for x in step_ms]
+    attn_ms = sum(steps_ms)
+    flops = w.rank_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    es = 2 if w.dtype == "bf16" else 4
+    part_bytes = 2 * w.b * w.s * (w.hq + 2 * w.hkv) * w.d * es + 4 * w.s
+    merge_rows = sum(st["rows"] for st in buf["steps"])
+    merge_bytes = w.b * w.hq * (4 * w.d + 4) * (merge_rows + 2 * w.c)
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    line = {
+        "metric": "causal attention fwd TFLOP/s + % bf16 MFMA peak, per-GPU CP share, s=32k",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded normal Q/K/V, resident in HBM)",
+        "config": {"workload": w.name, "b": w.b, "s": w.s, "hq": w.hq, "hkv": w.hkv,
+                   "d": w.d, "cp": w.cp, "rank": rank,
+                   "rope_theta": w.rope_theta},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "kernel": "attn_step_bf16" if w.dtype == "bf16" else "attn_step_f32"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "kernels_ms": {"partition_qkv": round(mean(part_ms), 4),
+                       "steps": [round(x, 4) for x in steps_ms],
+                       "merge": round(mean(merge_ms), 4)},
+        "attention_tflops": round(attn_tflops, 2),
+        "steps_plus_merge_tflops": round(flops / ((attn_ms + mean(merge_ms)) * 1e-3) / 1e12, 2),
+        "partition_gbps": round(part_bytes / (mean(part_ms) * 1e-3) / 1e9, 1),
+        "merge_gbps": round(merge_bytes / (mean(merge_ms) * 1e-3) / 1e9, 1),
+        "rank_flops": flops,
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+    }
+    if args.cpu_sample_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, rank, args.cpu_sample_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * cpattn - context-parallel blockwise causal attention, forward, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method ("Megatron-LM 篇", Context Parallel, sections 3.1-3.5; with
+ * "超大规模集群下大语言模型训练实操指南", section "CP 与其他技术结合"):
+ * the sequence is split over cp ranks; each rank computes FA2-style
+ * blockwise attention of its queries against one rank's keys and values per
+ * ring step, producing a partial output O_i and its log-sum-exp L_i; the L
+ * are corrected step by step and the O are rescaled and merged at the end,
+ * so each rank's result equals its slice of ordinary causal attention.
+ * On one GPU the ring exchange becomes a pointer hand-off: at step i rank r
+ * reads the partitioned K/V block of rank (r - i) mod cp.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Shapes (C order, innermost last):
+ *   q  [b, s, hq, d]        k, v  [b, s, hkv, d]          (unpartitioned)
+ *   xz [cp, b, 2c, h, d]    partitioned: rank r's rows at xz + r*b*2c*h*d
+ *   c = s / (2*cp) is the chunk length, 2c the rows a rank holds.
+ *   O_i, O  float or bf16 [b, rows, hq, d];  L_i, L  float [b, hq, rows]
+ * GQA: query head h reads KV head h / (hq/hkv) (contiguous groups).
+ * Softmax scale: 'scale' <= 0 selects 1/sqrt(d).
+ * L is the natural-log log-sum-exp of the scaled scores of a row.
+ *
+ * Ownership: the caller allocates and frees every device buffer; the
+ * library allocates no device memory and keeps no state between calls.
+ * Device pointers must be 16-byte aligned and must not overlap unless a
+ * function says otherwise.
+ *
+ * Streams: 'stream' is a hipStream_t (NULL = the default stream).  Device
+ * functions enqueue their kernels on it and return without synchronising;
+ * a device fault surfaces at the caller's next synchronisation.
+ *
+ * Errors: arguments are validated before anything is launched; a rejected
+ * call launches nothing and returns a nonzero status (cpattn_status_str
+ * names it).  CPATTN_EHIP reports a failed kernel launch.
+ *
+ * Thread safety: every function is reentrant; calls on different streams
+ * may run concurrently.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Problem dimensions. */
+typedef struct cpattn_dims {
+    int64_t b;    /* batch size, >= 1                                        */
+    int64_t s;    /* full sequence length, a multiple of 2*cp                 */
+    int32_t hq;   /* query heads, a multiple of hkv                           */
+    int32_t hkv;  /* key/value heads (GQA groups)                              */
+    int32_t d;    /* head dimension: 64 or 128                                 */
+    int32_t cp;   /* context-parallel size (ranks emulated), 1..64             */
+} cpattn_dims;
+
+/* Element types of Q, K, V (and of the merged output). */
+enum { CPATTN_F32 = 0, CPATTN_BF16 = 1 };
+
+/* Step modes ("Megatron-LM 篇" section 3.4). */
+enum {
+    CPATTN_CAUSAL = 0,        /* all 2c rows vs all 2c keys, key j <= row i  */
+    CPATTN_KV_FIRST_HALF = 1, /* all 2c rows vs keys 0..c-1, no mask          */
+    CPATTN_Q_SECOND_HALF = 2  /* rows c..2c-1 vs all 2c keys, no mask         */
+};
+
+/* Status codes. */
+enum {
+    CPATTN_OK = 0,
+    CPATTN_EINVAL = 1,   /* null pointer, bad enum, rank/step out of range   */
+    CPATTN_ESHAPE = 2,   /* s % 2cp, hq % hkv, unsupported d, b or s < 1     */
+    CPATTN_EDTYPE = 3,   /* dtype not supported by this entry point          */
+    CPATTN_EALIGN = 4,   /* a device pointer is not 16-byte aligned          */
+    CPATTN_ENOSPACE = 5, /* workspace too small                              */
+    CPATTN_EHIP = 6      /* the HIP runtime reported a launch error          */
+};
+
+/* Rotary position embedding applied during the split ("Megatron 面试题（一）",
+ * M016: RoPE rotates Q and K inside attention, and a CP rank must use the
+ * global position of each row).  Rotate-half form: for t < d/2 the pair
+ * (x[t], x[t + d/2]) is turned by pos * theta^(-2t/d) radians. */
+typedef struct cpattn_rope {
+    double theta;        /* base, > 0 (10000 for the usual RoPE)              */
+} cpattn_rope;
+
+/* One partial result of a step, as consumed by cpattn_merge. */
+typedef struct cpattn_partial {
+    const float *o;      /* [b, rows, hq, d] fp32, normalised within its step */
+    const float *lse;    /* [b, hq, rows] fp32 natural-log LSE                */
+    int64_t row0;        /* first local row this partial covers              */
+    int64_t rows;        /* number of local rows it covers                   */
+} cpattn_partial;
+
+#define CPATTN_MAX_PARTIALS 64
+#define CPATTN_MAX_MERGE_WEIGHTS 8192   /* hq * n per merge call */
+
+/* Mode and KV source of a step, host only, pure.
+ * "Megatron-LM 篇" 3.4: step 0 is causal; steps 1..rank drop the second
+ * half of the KV (CPATTN_KV_FIRST_HALF); later steps drop the first half of
+ * Q (CPATTN_Q_SECOND_HALF).  3.2 step 3: KV moves one hop along the ring per
+ * step, so at step i the rank holds rank (rank - i) mod cp's KV.
+ * Writes *mode and *src.  EINVAL if a pointer is NULL or step/rank are not
+ * in [0, cp). */
+int cpattn_step_mode(int step, int rank, int cp, int *mode, int *src);
+
+/* Global positions of rank 'rank''s 2c local rows, host only, pure.
+ * "Megatron-LM 篇" 3.4 and "超大规模集群下大语言模型训练实操指南" "CP 与其他技术
+ * 结合": chunk k is paired with chunk 2cp-1-k, rank r holds chunk r then
+ * chunk 2cp-1-r: pos[j] = r*c + j for j < c, (2cp-1-r)*c + j - c after.
+ * pos: caller-owned host array of 2c int32.  ESHAPE if s % (2cp) != 0 or
+ * 2c exceeds INT32_MAX; EINVAL for a NULL pointer or rank out of range. */
+int cpattn_partition_positions(int64_t s, int cp, int rank, int32_t *pos);
+
+/* Zigzag split of one tensor ("Megatron-LM 篇" 3.2 step 1), device.
+ * x [b, s, h, d] -> xz [cp, b, 2c, h, d] with xz[r, n, j] = x[n, pos_r[j]].
+ * dtype: CPATTN_F32 or CPATTN_BF16 (elements are copied bit for bit).
+ * pos_dev: optional device array [cp, 2c] int32 receiving every rank's
+ * positions (NULL to skip).  rope: optional; when given, each copied row is
+ * rotated at its global position (angles in fp64, rotation in fp32, result
+ * rounded to the element type).  h is the head count of this tensor (hq for
+ * Q, hkv for K and V); dims->hq/hkv are not used here.  x and xz must not
+ * overlap. */
+int cpattn_partition(const cpattn_dims *dims, int dtype, int h, const void *x,
+                     void *xz, int32_t *pos_dev, const cpattn_rope *rope,
+                     void *stream);
+
+/* One step's blockwise attention ("Megatron-LM 篇" 3.2 step 2 and 3.4),
+ * device.  q_r: rank's partitioned Q block [b, 2c, hq, d]; k_src, v_src:
+ * the source rank's partitioned K and V blocks [b, 2c, hkv, d].  All three
+ * have element type 'dtype' (CPATTN_BF16: bf16 MFMA with fp32 accumulation,
+ * d = 128; CPATTN_F32: fp32 throughout, the debug path, d = 64 or 128).  mode: CPATTN_CAUSAL,
+ * CPATTN_KV_FIRST_HALF or CPATTN_Q_SECOND_HALF.
+ * Writes o [b, rows, hq, d] fp32 (normalised within the step) and
+ * lse [b, hq, rows] fp32, rows = 2c (first two modes) or c (the last one,
+ * holding local rows c..2c-1).  d: 64 or 128. */
+int cpattn_step_fwd(const cpattn_dims *dims, int dtype, float scale, int mode,
+                    const void *q_r, const void *k_src, const void *v_src,
+                    float *o, float *lse, void *stream);
+
+/* LSE correction and merge of n partials ("Megatron-LM 篇" 3.2 steps 4 and
+ * 5), device.  For each batch n, local row j in [0, 2c) and head h, over the
+ * partials that cover j: M = max L_p, L = M + ln sum_p exp(L_p - M),
+ * O = sum_p exp(L_p - L) O_p.  A row no partial covers gets L = -inf, O = 0.
+ * p: host array of n descriptors (device pointers inside), 1 <= n <=
+ * CPATTN_MAX_PARTIALS and hq * n <= CPATTN_MAX_MERGE_WEIGHTS (ESHAPE
+ * otherwise); each partial's rows must lie inside [0, 2c).  out_dtype: CPATTN_F32 or CPATTN_BF16 (round to
+ * nearest even).  o_out [b, 2c, hq, d]; lse_out [b, hq, 2c] fp32 or NULL. */
+int cpattn_merge(const cpattn_dims *dims, int n, const cpattn_partial *p,
+                 int out_dtype, void *o_out, float *lse_out, void *stream);
+
+/* Bytes of device workspace cpattn_forward needs for 'rank' (the fp32
+ * partials of all cp steps).  Returns 0 on invalid dims or rank. */
+size_t cpattn_forward_workspace(const cpattn_dims *dims, int rank);
+
+/* One rank's whole forward share, device: the cp steps of
+ * cpattn_step_mode, each reading the source rank's K/V block of the
+ * partitioned qz/kz/vz ([cp, b, 2c, h, d] as written by cpattn_partition),
+ * then cpattn_merge into o_out [b, 2c, hq, d] (out_dtype) and lse_out
+ * [b, hq, 2c] (may be NULL).  ws: device workspace of at least
+ * cpattn_forward_workspace bytes (ENOSPACE otherwise), 256-byte aligned. */
+int cpattn_forward(const cpattn_dims *dims, int dtype, float scale, int rank,
+                   const void *qz, const void *kz, const void *vz, void *ws,
+                   size_t ws_bytes, int out_dtype, void *o_out, float *lse_out,
+                   void *stream);
+
+/* Static name of a status code. */
+const char *cpattn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

@@ -1,0 +1,159 @@
+"""ctypes binding of ``libcpattn.so`` (declared in ``include/cpattn.h``).
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name.  Device buffers are torch tensors (their ``data_ptr()``) or
+raw integer addresses; ``stream`` is a ``torch.cuda.Stream``, a raw
+``hipStream_t`` integer, or None for torch's current stream.  A nonzero
+status raises :class:`CpattnError`.  There is no fallback: if the library
+is not built, every call raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpattn.so")
+
+CPATTN_F32 = 0
+CPATTN_BF16 = 1
+CPATTN_CAUSAL = 0
+CPATTN_KV_FIRST_HALF = 1
+CPATTN_Q_SECOND_HALF = 2
+CPATTN_OK, CPATTN_EINVAL, CPATTN_ESHAPE, CPATTN_EDTYPE, CPATTN_EALIGN, \
+    CPATTN_ENOSPACE, CPATTN_EHIP = range(7)
+CPATTN_MAX_PARTIALS = 64
+
+
+class cpattn_dims(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("s", ctypes.c_int64), ("hq", ctypes.c_int32),
+                ("hkv", ctypes.c_int32), ("d", ctypes.c_int32), ("cp", ctypes.c_int32)]
+
+
+class cpattn_rope(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_double)]
+
+
+class cpattn_partial(ctypes.Structure):
+    _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("row0", ctypes.c_int64), ("rows", ctypes.c_int64)]
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, status, func):
+        self.status = status
+        super().__init__(f"{func}: {cpattn_status_str(status)}")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m long_context_causal_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        D = ctypes.POINTER(cpattn_dims)
+        L.cpattn_step_mode.argtypes = [I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+        L.cpattn_partition_positions.argtypes = [ctypes.c_int64, I, I,
+                                                 ctypes.POINTER(ctypes.c_int32)]
+        L.cpattn_partition.argtypes = [D, I, I, P, P, P, ctypes.POINTER(cpattn_rope), P]
+        L.cpattn_step_fwd.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P]
+        L.cpattn_merge.argtypes = [D, I, ctypes.POINTER(cpattn_partial), I, P, P, P]
+        L.cpattn_forward_workspace.argtypes = [D, I]
+        L.cpattn_forward_workspace.restype = ctypes.c_size_t
+        L.cpattn_forward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, ctypes.c_size_t,
+                                     I, P, P, P]
+        L.cpattn_status_str.argtypes = [I]
+        L.cpattn_status_str.restype = ctypes.c_char_p
+        for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
+                     "cpattn_step_fwd", "cpattn_merge", "cpattn_forward"):
+            getattr(L, name).restype = I
+        _lib = L
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, func):
+    if status != CPATTN_OK:
+        raise CpattnError(status, func)
+
+
+def make_dims(b, s, hq, hkv, d, cp):
+    return cpattn_dims(b, s, hq, hkv, d, cp)
+
+
+def cpattn_status_str(status):
+    return lib().cpattn_status_str(int(status)).decode()
+
+
+def cpattn_step_mode(step, rank, cp):
+    mode, src = ctypes.c_int(), ctypes.c_int()
+    _check(lib().cpattn_step_mode(step, rank, cp, ctypes.byref(mode), ctypes.byref(src)),
+           "cpattn_step_mode")
+    return mode.value, src.value
+
+
+def cpattn_partition_positions(s, cp, rank):
+    if s % (2 * cp) != 0:
+        raise CpattnError(CPATTN_ESHAPE, "cpattn_partition_positions")
+    out = np.empty(s // cp, dtype=np.int32)
+    _check(lib().cpattn_partition_positions(
+        s, cp, rank, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+        "cpattn_partition_positions")
+    return out
+
+
+def cpattn_partition(dims, dtype, h, x, xz, pos=None, rope_theta=None, stream=None):
+    rope = ctypes.byref(cpattn_rope(rope_theta)) if rope_theta is not None else None
+    _check(lib().cpattn_partition(ctypes.byref(dims), dtype, h, _ptr(x), _ptr(xz), _ptr(pos),
+                                  rope, _stream(stream)), "cpattn_partition")
+
+
+def cpattn_step_fwd(dims, dtype, scale, mode, q_r, k_src, v_src, o, lse, stream=None):
+    _check(lib().cpattn_step_fwd(ctypes.byref(dims), dtype, float(scale), mode, _ptr(q_r),
+                                 _ptr(k_src), _ptr(v_src), _ptr(o), _ptr(lse),
+                                 _stream(stream)), "cpattn_step_fwd")
+
+
+def cpattn_merge(dims, partials, out_dtype, o_out, lse_out=None, stream=None):
+    """partials: sequence of (o, lse, row0, rows)."""
+    arr = (cpattn_partial * max(1, len(partials)))()
+    for i, (o, lse, row0, rows) in enumerate(partials):
+        arr[i] = cpattn_partial(_ptr(o), _ptr(lse), row0, rows)
+    _check(lib().cpattn_merge(ctypes.byref(dims), len(partials), arr, out_dtype, _ptr(o_out),
+                              _ptr(lse_out), _stream(stream)), "cpattn_merge")
+
+
+def cpattn_forward_workspace(dims, rank):
+    return int(lib().cpattn_forward_workspace(ctypes.byref(dims), rank))
+
+
+def cpattn_forward(dims, dtype, scale, rank, qz, kz, vz, ws, ws_bytes, out_dtype, o_out,
+                   lse_out=None, stream=None):
+    _check(lib().cpattn_forward(ctypes.byref(dims), dtype, float(scale), rank, _ptr(qz),
+                                _ptr(kz), _ptr(vz), _ptr(ws), int(ws_bytes), out_dtype,
+                                _ptr(o_out), _ptr(lse_out), _stream(stream)),
+           "cpattn_forward")

@@ -1,0 +1,238 @@
+// C ABI of cpattn: argument validation, the step schedule, workspace
+// layout and the launch sequence of one rank's forward share.  See
+// include/cpattn.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "cpattn.h"
+#include "internal.h"
+
+namespace cpattn {
+
+StepGeom step_geom(const cpattn_dims &dims, int mode, float scale) {
+    StepGeom g;
+    const int64_t c = dims.s / (2 * dims.cp);
+    g.b = dims.b;
+    g.two_c = 2 * c;
+    g.hq = dims.hq;
+    g.hkv = dims.hkv;
+    g.d = dims.d;
+    g.causal = mode == CPATTN_CAUSAL;
+    g.q_row0 = mode == CPATTN_Q_SECOND_HALF ? c : 0;
+    g.nq = mode == CPATTN_Q_SECOND_HALF ? c : 2 * c;
+    g.nk = mode == CPATTN_KV_FIRST_HALF ? c : 2 * c;
+    g.scale = scale > 0.0f ? scale : (float)(1.0 / sqrt((double)dims.d));
+    g.scale_log2 = (float)((double)g.scale * 1.4426950408889634);
+    return g;
+}
+
+}  // namespace cpattn
+
+namespace {
+
+using cpattn::StepGeom;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by the device entry points.
+int check_dims(const cpattn_dims *dims) {
+    if (dims == nullptr) return CPATTN_EINVAL;
+    if (dims->b < 1 || dims->s < 1 || dims->hq < 1 || dims->hkv < 1 || dims->cp < 1)
+        return CPATTN_ESHAPE;
+    if (dims->cp > CPATTN_MAX_PARTIALS) return CPATTN_ESHAPE;
+    if (dims->s % (2 * (int64_t)dims->cp) != 0) return CPATTN_ESHAPE;
+    if (dims->hq % dims->hkv != 0) return CPATTN_ESHAPE;
+    if (dims->d != 64 && dims->d != 128) return CPATTN_ESHAPE;
+    // row indices inside the kernels are 32-bit
+    if (dims->s / dims->cp > INT32_MAX / 2) return CPATTN_ESHAPE;
+    if (dims->b * dims->s > (int64_t)1 << 40) return CPATTN_ESHAPE;
+    return CPATTN_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? CPATTN_OK : CPATTN_EHIP; }
+
+int64_t step_rows(const cpattn_dims &d, int mode) {
+    const int64_t c = d.s / (2 * d.cp);
+    return mode == CPATTN_Q_SECOND_HALF ? c : 2 * c;
+}
+
+// Bytes of one step's partial (O then LSE), each rounded up to 256 bytes.
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t partial_o_bytes(const cpattn_dims &d, int64_t rows) {
+    return round256((size_t)d.b * rows * d.hq * d.d * sizeof(float));
+}
+size_t partial_l_bytes(const cpattn_dims &d, int64_t rows) {
+    return round256((size_t)d.b * d.hq * rows * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *cpattn_status_str(int status) {
+    switch (status) {
+        case CPATTN_OK: return "CPATTN_OK";
+        case CPATTN_EINVAL: return "CPATTN_EINVAL: invalid argument";
+        case CPATTN_ESHAPE: return "CPATTN_ESHAPE: unsupported shape";
+        case CPATTN_EDTYPE: return "CPATTN_EDTYPE: unsupported dtype";
+        case CPATTN_EALIGN: return "CPATTN_EALIGN: pointer not 16-byte aligned";
+        case CPATTN_ENOSPACE: return "CPATTN_ENOSPACE: workspace too small";
+        case CPATTN_EHIP: return "CPATTN_EHIP: HIP launch error";
+        default: return "CPATTN_UNKNOWN";
+    }
+}
+
+int cpattn_step_mode(int step, int rank, int cp, int *mode, int *src) {
+    if (mode == nullptr || src == nullptr) return CPATTN_EINVAL;
+    if (cp < 1 || rank < 0 || rank >= cp || step < 0 || step >= cp) return CPATTN_EINVAL;
+    *src = ((rank - step) % cp + cp) % cp;
+    if (step == 0)
+        *mode = CPATTN_CAUSAL;
+    else if (step <= rank)
+        *mode = CPATTN_KV_FIRST_HALF;
+    else
+        *mode = CPATTN_Q_SECOND_HALF;
+    return CPATTN_OK;
+}
+
+int cpattn_partition_positions(int64_t s, int cp, int rank, int32_t *pos) {
+    if (pos == nullptr || cp < 1 || rank < 0 || rank >= cp) return CPATTN_EINVAL;
+    if (s < 1 || s % (2 * (int64_t)cp) != 0) return CPATTN_ESHAPE;
+    const int64_t c = s / (2 * (int64_t)cp);
+    if (2 * c > INT32_MAX || s > INT32_MAX) return CPATTN_ESHAPE;
+    const int64_t big = 2 * (int64_t)cp - 1 - rank;
+    for (int64_t j = 0; j < c; ++j) pos[j] = (int32_t)(rank * c + j);
+    for (int64_t j = 0; j < c; ++j) pos[c + j] = (int32_t)(big * c + j);
+    return CPATTN_OK;
+}
+
+int cpattn_partition(const cpattn_dims *dims, int dtype, int h, const void *x, void *xz,
+                     int32_t *pos_dev, const cpattn_rope *rope, void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if (x == nullptr || xz == nullptr) return CPATTN_EINVAL;
+    if (h < 1) return CPATTN_ESHAPE;
+    if (!aligned16(x) || !aligned16(xz) || (pos_dev && ((uintptr_t)pos_dev & 3u)))
+        return CPATTN_EALIGN;
+    if (rope != nullptr && !(rope->theta > 0.0)) return CPATTN_EINVAL;
+    if (dims->s > INT32_MAX) return CPATTN_ESHAPE;
+    return status_of(cpattn::launch_partition(*dims, dtype, h, x, xz, pos_dev, rope,
+                                              (hipStream_t)stream));
+}
+
+int cpattn_step_fwd(const cpattn_dims *dims, int dtype, float scale, int mode,
+                    const void *q_r, const void *k_src, const void *v_src, float *o,
+                    float *lse, void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (mode != CPATTN_CAUSAL && mode != CPATTN_KV_FIRST_HALF && mode != CPATTN_Q_SECOND_HALF)
+        return CPATTN_EINVAL;
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if (dtype == CPATTN_BF16 && dims->d != 128) return CPATTN_ESHAPE;
+    if (!q_r || !k_src || !v_src || !o || !lse) return CPATTN_EINVAL;
+    if (!aligned16(q_r) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(o) ||
+        ((uintptr_t)lse & 3u))
+        return CPATTN_EALIGN;
+    if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
+    const StepGeom g = cpattn::step_geom(*dims, mode, scale);
+    // grid size must fit in 32 bits
+    if ((g.nq + 127) / 128 * g.hq * g.b > (int64_t)INT32_MAX) return CPATTN_ESHAPE;
+    hipError_t e = dtype == CPATTN_BF16
+                       ? cpattn::launch_step_bf16(g, q_r, k_src, v_src, o, lse, (hipStream_t)stream)
+                       : cpattn::launch_step_f32(g, q_r, k_src, v_src, o, lse, (hipStream_t)stream);
+    return status_of(e);
+}
+
+int cpattn_merge(const cpattn_dims *dims, int n, const cpattn_partial *p, int out_dtype,
+                 void *o_out, float *lse_out, void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (p == nullptr || o_out == nullptr) return CPATTN_EINVAL;
+    if (n < 1 || n > CPATTN_MAX_PARTIALS) return CPATTN_ESHAPE;
+    if ((int64_t)dims->hq * n > CPATTN_MAX_MERGE_WEIGHTS) return CPATTN_ESHAPE;
+    if (out_dtype != CPATTN_F32 && out_dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    const int64_t two_c = dims->s / dims->cp;
+    for (int i = 0; i < n; ++i) {
+        if (p[i].o == nullptr || p[i].lse == nullptr) return CPATTN_EINVAL;
+        if (p[i].row0 < 0 || p[i].rows < 1 || p[i].row0 + p[i].rows > two_c) return CPATTN_ESHAPE;
+        if (!aligned16(p[i].o) || ((uintptr_t)p[i].lse & 3u)) return CPATTN_EALIGN;
+    }
+    if (!aligned16(o_out) || (lse_out && ((uintptr_t)lse_out & 3u))) return CPATTN_EALIGN;
+    if (dims->b * two_c > (int64_t)INT32_MAX) return CPATTN_ESHAPE;
+    cpattn::MergeArgs a;
+    a.b = dims->b;
+    a.two_c = two_c;
+    a.hq = dims->hq;
+    a.d = dims->d;
+    a.n = n;
+    a.parts = p;
+    a.out_dtype = out_dtype;
+    a.o_out = o_out;
+    a.lse_out = lse_out;
+    return status_of(cpattn::launch_merge(a, (hipStream_t)stream));
+}
+
+size_t cpattn_forward_workspace(const cpattn_dims *dims, int rank) {
+    if (check_dims(dims) != CPATTN_OK || rank < 0 || rank >= dims->cp) return 0;
+    size_t total = 0;
+    for (int i = 0; i < dims->cp; ++i) {
+        int mode, src;
+        cpattn_step_mode(i, rank, dims->cp, &mode, &src);
+        const int64_t rows = step_rows(*dims, mode);
+        total += partial_o_bytes(*dims, rows) + partial_l_bytes(*dims, rows);
+    }
+    return total;
+}
+
+int cpattn_forward(const cpattn_dims *dims, int dtype, float scale, int rank, const void *qz,
+                   const void *kz, const void *vz, void *ws, size_t ws_bytes, int out_dtype,
+                   void *o_out, float *lse_out, void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (rank < 0 || rank >= dims->cp) return CPATTN_EINVAL;
+    if (!qz || !kz || !vz || !ws || !o_out) return CPATTN_EINVAL;
+    if (((uintptr_t)ws & 255u) != 0) return CPATTN_EALIGN;
+    if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if (out_dtype != CPATTN_F32 && out_dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if (dtype == CPATTN_BF16 && dims->d != 128) return CPATTN_ESHAPE;
+    if ((int64_t)dims->hq * dims->cp > CPATTN_MAX_MERGE_WEIGHTS) return CPATTN_ESHAPE;
+    if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz) || !aligned16(o_out) ||
+        (lse_out && ((uintptr_t)lse_out & 3u)))
+        return CPATTN_EALIGN;
+    const size_t need = cpattn_forward_workspace(dims, rank);
+    if (ws_bytes < need) return CPATTN_ENOSPACE;
+
+    const size_t es = dtype == CPATTN_BF16 ? 2 : 4;
+    const int64_t two_c = dims->s / dims->cp;
+    const size_t q_block = (size_t)dims->b * two_c * dims->hq * dims->d * es;
+    const size_t kv_block = (size_t)dims->b * two_c * dims->hkv * dims->d * es;
+    const char *q_r = (const char *)qz + rank * q_block;
+
+    cpattn_partial parts[CPATTN_MAX_PARTIALS];
+    char *cursor = (char *)ws;
+    for (int i = 0; i < dims->cp; ++i) {
+        int mode, src;
+        cpattn_step_mode(i, rank, dims->cp, &mode, &src);
+        const int64_t rows = step_rows(*dims, mode);
+        float *o = (float *)cursor;
+        cursor += partial_o_bytes(*dims, rows);
+        float *lse = (float *)cursor;
+        cursor += partial_l_bytes(*dims, rows);
+        // ring hand-off: step i reads rank src's partitioned K/V block
+        const char *k_src = (const char *)kz + src * kv_block;
+        const char *v_src = (const char *)vz + src * kv_block;
+        st = cpattn_step_fwd(dims, dtype, scale, mode, q_r, k_src, v_src, o, lse, stream);
+        if (st) return st;
+        parts[i].o = o;
+        parts[i].lse = lse;
+        parts[i].row0 = mode == CPATTN_Q_SECOND_HALF ? two_c / 2 : 0;
+        parts[i].rows = rows;
+    }
+    return cpattn_merge(dims, dims->cp, parts, out_dtype, o_out, lse_out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by api.cpp and
+// returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cpattn.h"
+
+namespace cpattn {
+
+// Geometry of one step, derived from the dims and the mode.
+struct StepGeom {
+    int64_t b;
+    int64_t two_c;      // rows of a rank's local block
+    int32_t hq, hkv, d;
+    int64_t q_row0;     // first local query row read
+    int64_t nq;         // query rows computed (= rows of O_i)
+    int64_t nk;         // keys visible to the step (0..nk-1 of the block)
+    bool causal;        // key j visible to row i only if j <= q_row0 + i
+    float scale;        // softmax scale
+    float scale_log2;   // softmax scale * log2(e)
+};
+
+StepGeom step_geom(const cpattn_dims &dims, int mode, float scale);
+
+hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h,
+                            const void *x, void *xz, int32_t *pos,
+                            const cpattn_rope *rope, hipStream_t stream);
+
+hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k,
+                            const void *v, float *o, float *lse,
+                            hipStream_t stream);
+
+hipError_t launch_step_f32(const StepGeom &g, const void *q, const void *k,
+                           const void *v, float *o, float *lse,
+                           hipStream_t stream);
+
+struct MergeArgs {
+    int64_t b, two_c;
+    int32_t hq, d;
+    int n;
+    const cpattn_partial *parts;   // host array, n entries
+    int out_dtype;
+    void *o_out;
+    float *lse_out;
+};
+
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
+
+}  // namespace cpattn

@@ -1,0 +1,186 @@
+// Zigzag split of Q, K or V over the cp emulated ranks, with global
+// position ids and optional RoPE at those positions.
+//
+// "Megatron-LM 篇", Context Parallel 3.2 step 1 (split by cp_size) and 3.4
+// (rank_0 trades half its data with rank_n-1, rank_1 with rank_n-2, ...);
+// "超大规模集群下大语言模型训练实操指南", "CP 与其他技术结合" (one big and one
+// small attention per device).  The sequence is cut into 2cp chunks of c
+// rows; rank r holds chunk r, then chunk 2cp-1-r:
+//     xz[r, n, j] = x[n, pos_r(j)],  pos_r(j) = r*c + j            (j < c)
+//                                             (2cp-1-r)*c + j - c  (j >= c)
+// RoPE ("Megatron 面试题（一）", M016): every copied row is rotated at its
+// global position pos_r(j), never at its local index.
+//
+// Without RoPE the kernel is a pure HBM copy: each workgroup moves a run of
+// whole output rows with 16-byte loads and stores, consecutive lanes on
+// consecutive addresses.  With RoPE each workgroup first builds the row's
+// cos/sin table in LDS (angles pos * theta^(-2t/d) in fp64, sincos in fp64,
+// rounded to fp32), then rotates the pairs (t, t + d/2) of every head in
+// fp32 and rounds the result to the element type (bf16: nearest even).
+#include "internal.h"
+
+#include <math.h>
+
+namespace cpattn {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int NT = 256;
+
+struct CopyParams {
+    const char *x;
+    char *xz;
+    int32_t *pos;
+    int64_t s, c, b, rows_total;   // rows_total = cp * b * 2c
+    int cp;
+    int vecs_per_row;              // 16-byte vectors per row (h*d*es/16)
+    int rows_per_block;
+};
+
+__device__ __forceinline__ int64_t global_pos(int64_t r, int64_t j, int64_t c, int cp) {
+    return j < c ? r * c + j : (2 * cp - 1 - r) * c + (j - c);
+}
+
+// Output row index -> (rank, batch, local row)
+__device__ __forceinline__ void split_row(int64_t row, int64_t b, int64_t two_c,
+                                          int64_t &r, int64_t &n, int64_t &j) {
+    j = row % two_c;
+    int64_t rn = row / two_c;
+    n = rn % b;
+    r = rn / b;
+}
+
+__global__ void __launch_bounds__(NT) partition_copy(CopyParams p) {
+    const int64_t row0 = (int64_t)blockIdx.x * p.rows_per_block;
+    const int64_t two_c = 2 * p.c;
+    const int nvec = p.rows_per_block * p.vecs_per_row;
+    for (int i = threadIdx.x; i < nvec; i += NT) {
+        const int rr = i / p.vecs_per_row;
+        const int vv = i - rr * p.vecs_per_row;
+        const int64_t row = row0 + rr;
+        if (row >= p.rows_total) break;
+        int64_t r, n, j;
+        split_row(row, p.b, two_c, r, n, j);
+        const int64_t src_row = n * p.s + global_pos(r, j, p.c, p.cp);
+        const u32x4 *src = (const u32x4 *)p.x + src_row * p.vecs_per_row + vv;
+        u32x4 *dst = (u32x4 *)p.xz + row * p.vecs_per_row + vv;
+        *dst = *src;
+    }
+    if (p.pos != nullptr && blockIdx.x == 0) {
+        // positions of every rank: pos[r*2c + j]
+        const int64_t total = (int64_t)p.cp * two_c;
+        for (int64_t i = threadIdx.x; i < total; i += NT)
+            p.pos[i] = (int32_t)global_pos(i / two_c, i % two_c, p.c, p.cp);
+    }
+}
+
+template <typename T>
+struct RopeParams {
+    const T *x;
+    T *xz;
+    int32_t *pos;
+    int64_t s, c, b, rows_total;
+    int cp, h, d;
+    double theta;
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
+    return __uint_as_float((unsigned)v << 16);
+}
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
+    __bf16 b = (__bf16)v;   // round to nearest even
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+// One output row per loop iteration of the workgroup.
+template <typename T>
+__global__ void __launch_bounds__(NT) partition_rope(RopeParams<T> p) {
+    extern __shared__ float cs[];   // [d/2] cos, then [d/2] sin
+    const int half = p.d / 2;
+    const int64_t two_c = 2 * p.c;
+    for (int64_t row = blockIdx.x; row < p.rows_total; row += gridDim.x) {
+        int64_t r, n, j;
+        split_row(row, p.b, two_c, r, n, j);
+        const int64_t gp = global_pos(r, j, p.c, p.cp);
+        __syncthreads();
+        for (int t = threadIdx.x; t < half; t += NT) {
+            const double inv_freq = pow(p.theta, -2.0 * (double)t / (double)p.d);
+            double sn, cn;
+            sincos((double)gp * inv_freq, &sn, &cn);
+            cs[t] = (float)cn;
+            cs[half + t] = (float)sn;
+        }
+        __syncthreads();
+        const T *src = p.x + (n * p.s + gp) * (int64_t)p.h * p.d;
+        T *dst = p.xz + row * (int64_t)p.h * p.d;
+        for (int i = threadIdx.x; i < p.h * half; i += NT) {
+            const int hh = i / half, t = i - hh * half;
+            const float x1 = to_f32(src[hh * p.d + t]);
+            const float x2 = to_f32(src[hh * p.d + half + t]);
+            const float cn = cs[t], sn = cs[half + t];
+            dst[hh * p.d + t] = from_f32<T>(x1 * cn - x2 * sn);
+            dst[hh * p.d + half + t] = from_f32<T>(x2 * cn + x1 * sn);
+        }
+    }
+    if (p.pos != nullptr && blockIdx.x == 0) {
+        const int64_t total = (int64_t)p.cp * two_c;
+        for (int64_t i = threadIdx.x; i < total; i += NT)
+            p.pos[i] = (int32_t)global_pos(i / two_c, i % two_c, p.c, p.cp);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const void *x,
+                            void *xz, int32_t *pos, const cpattn_rope *rope,
+                            hipStream_t stream) {
+    const int es = dtype == CPATTN_BF16 ? 2 : 4;
+    const int64_t c = dims.s / (2 * dims.cp);
+    const int64_t rows_total = (int64_t)dims.cp * dims.b * 2 * c;
+    if (rope == nullptr) {
+        CopyParams p;
+        p.x = (const char *)x;
+        p.xz = (char *)xz;
+        p.pos = pos;
+        p.s = dims.s;
+        p.c = c;
+        p.b = dims.b;
+        p.rows_total = rows_total;
+        p.cp = dims.cp;
+        p.vecs_per_row = (int)((int64_t)h * dims.d * es / 16);
+        // about 64 KiB per workgroup
+        p.rows_per_block = p.vecs_per_row >= 4096 ? 1 : 4096 / p.vecs_per_row;
+        const int64_t blocks = (rows_total + p.rows_per_block - 1) / p.rows_per_block;
+        hipLaunchKernelGGL(partition_copy, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
+        return hipGetLastError();
+    }
+    const int64_t blocks = rows_total < 65536 ? rows_total : 65536;
+    const size_t shmem = sizeof(float) * dims.d;
+    if (dtype == CPATTN_BF16) {
+        RopeParams<uint16_t> p{(const uint16_t *)x, (uint16_t *)xz, pos, dims.s, c, dims.b,
+                               rows_total, dims.cp, h, dims.d, rope->theta};
+        hipLaunchKernelGGL(partition_rope<uint16_t>, dim3((unsigned)blocks), dim3(NT), shmem,
+                           stream, p);
+    } else {
+        RopeParams<float> p{(const float *)x, (float *)xz, pos, dims.s, c, dims.b,
+                            rows_total, dims.cp, h, dims.d, rope->theta};
+        hipLaunchKernelGGL(partition_rope<float>, dim3((unsigned)blocks), dim3(NT), shmem,
+                           stream, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cpattn

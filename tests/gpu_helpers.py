@@ -1,0 +1,87 @@
+"""Shared helpers of the GPU parity tests (not collected by pytest)."""
+import dataclasses
+
+import numpy as np
+import torch
+
+from long_context_causal_amd import cpattn as C
+from long_context_causal_amd.inputs import Workload, as_f32, make_inputs
+from long_context_causal_amd.runner import CPProblem, bf16_bits, to_device
+from oracle import attention_rows, causal_attention
+from oracle import cp as ocp
+
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_ABS = 2e-3
+F32_MAX_ABS = 1e-5
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def host_f32(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        from long_context_causal_amd.inputs import bf16_bits_to_f32
+        return bf16_bits_to_f32(bf16_bits(t))
+    return t.detach().float().cpu().numpy()
+
+
+def errors(got, want):
+    diff = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    return float(diff.max()), float(diff.mean())
+
+
+def assert_close(name, got, want, max_abs, mean_abs=None):
+    mx, mn = errors(got, want)
+    say(f"  [{name}] max_abs={mx:.3e} mean_abs={mn:.3e} (bounds {max_abs:g}"
+        f"{'' if mean_abs is None else f', mean {mean_abs:g}'})")
+    assert np.isfinite(np.asarray(got)).all(), f"{name}: non-finite output"
+    assert mx <= max_abs, f"{name}: max abs {mx} > {max_abs}"
+    if mean_abs is not None:
+        assert mn <= mean_abs, f"{name}: mean abs {mn} > {mean_abs}"
+
+
+def small(w: Workload, s: int, b=None) -> Workload:
+    """The same workload (heads, d, cp, dtype, distribution) at length s."""
+    return dataclasses.replace(w, s=s, b=w.b if b is None else b)
+
+
+def oracle_full(w: Workload, q, k, v):
+    """Non-CP oracle (O [b, s, hq, d], L [b, hq, s]) in fp64, RoPE applied."""
+    qf, kf, vf = (as_f32(x).astype(np.float64) for x in (q, k, v))
+    if w.rope_theta is not None:
+        ar = np.arange(qf.shape[1])
+        qf, kf = ocp.rope(qf, ar, w.rope_theta), ocp.rope(kf, ar, w.rope_theta)
+    return causal_attention(qf, kf, vf)
+
+
+def run_rank(P: CPProblem, rank, out_dtype=C.CPATTN_F32):
+    buf = P.alloc_rank(rank, out_dtype)
+    P.forward(buf)
+    torch.cuda.synchronize()
+    return host_f32(buf["o"]), buf["lse"].cpu().numpy()
+
+
+def oracle_sampled_rows(w: Workload, q, k, v, positions):
+    """Oracle output of the global rows ``positions`` (all heads)."""
+    positions = np.asarray(positions)
+    qf = as_f32(q[:, positions]).astype(np.float64)
+    hi = int(positions.max()) + 1
+    kf = as_f32(k[:, :hi]).astype(np.float64)
+    vf = as_f32(v[:, :hi]).astype(np.float64)
+    if w.rope_theta is not None:
+        qf = ocp.rope(qf, positions, w.rope_theta)
+        kf = ocp.rope(kf, np.arange(hi), w.rope_theta)
+    return attention_rows(qf, kf, vf, positions + 1)
+
+
+def sample_local_rows(c, n_mid, seed):
+    """Local row indices: both chunk edges plus n_mid random rows."""
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, c - 1, c, c + 1, 2 * c - 1]
+    mid = rng.choice(2 * c, size=n_mid, replace=False)
+    return np.unique(np.concatenate([edges, mid]))
+
+
+__all__ = ["C", "CPProblem", "Workload", "make_inputs", "to_device", "torch", "np", "ocp",
+           "attention_rows", "causal_attention", "as_f32"]

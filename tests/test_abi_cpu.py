@@ -1,0 +1,162 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+its pure host functions agree bit for bit with the oracle, and invalid
+arguments are rejected with the documented status before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from long_context_causal_amd import build as cbuild
+from long_context_causal_amd import cpattn as C
+from oracle import cp as ocp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    cbuild.ensure_built()
+    yield
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "cpattn.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpattn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 8
+    lib = ctypes.CDLL(C.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for st in range(7):
+        assert C.cpattn_status_str(st).startswith("CPATTN_")
+    assert "UNKNOWN" in C.cpattn_status_str(99)
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8, 16])
+def test_step_mode_matches_oracle(cp):
+    for r in range(cp):
+        for i in range(cp):
+            assert C.cpattn_step_mode(i, r, cp) == ocp.step_schedule(i, r, cp)
+
+
+def test_step_mode_rejects():
+    for args in [(0, 0, 0), (2, 0, 2), (0, 2, 2), (-1, 0, 2)]:
+        with pytest.raises(C.CpattnError) as e:
+            C.cpattn_step_mode(*args)
+        assert e.value.status == C.CPATTN_EINVAL
+    assert C.lib().cpattn_step_mode(0, 0, 1, None, None) == C.CPATTN_EINVAL
+
+
+@pytest.mark.parametrize("s,cp", [(8, 2), (16, 4), (512, 2), (32768, 8), (131072, 16),
+                                  (96, 6)])
+def test_positions_bit_exact_vs_oracle(s, cp):
+    for r in range(cp):
+        got = C.cpattn_partition_positions(s, cp, r)
+        assert got.dtype == np.int32
+        assert np.array_equal(got, ocp.zigzag_positions(s, cp, r))
+
+
+def test_positions_rejects():
+    buf = (ctypes.c_int32 * 16)()
+    L = C.lib()
+    assert L.cpattn_partition_positions(10, 3, 0, buf) == C.CPATTN_ESHAPE
+    assert L.cpattn_partition_positions(8, 2, 2, buf) == C.CPATTN_EINVAL
+    assert L.cpattn_partition_positions(8, 2, 0, None) == C.CPATTN_EINVAL
+
+
+def _dims(**kw):
+    base = dict(b=1, s=512, hq=4, hkv=4, d=64, cp=2)
+    base.update(kw)
+    return C.make_dims(**base)
+
+
+ALIGNED = 1 << 20          # never dereferenced: validation fails first
+
+
+def _step(dims, dtype=C.CPATTN_F32, mode=C.CPATTN_CAUSAL, ptrs=None, scale=0.0):
+    p = ptrs or [ALIGNED] * 5
+    return C.lib().cpattn_step_fwd(ctypes.byref(dims), dtype, scale, mode, *p, 0)
+
+
+def test_step_fwd_validation_before_launch():
+    assert _step(_dims(s=510)) == C.CPATTN_ESHAPE                 # s % 2cp
+    assert _step(_dims(hq=6, hkv=4)) == C.CPATTN_ESHAPE           # hq % hkv
+    assert _step(_dims(d=96)) == C.CPATTN_ESHAPE                  # head dim
+    assert _step(_dims(d=64), dtype=C.CPATTN_BF16) == C.CPATTN_ESHAPE
+    assert _step(_dims(b=0)) == C.CPATTN_ESHAPE
+    assert _step(_dims(), dtype=7) == C.CPATTN_EDTYPE
+    assert _step(_dims(), mode=3) == C.CPATTN_EINVAL
+    assert _step(_dims(), ptrs=[0, ALIGNED, ALIGNED, ALIGNED, ALIGNED]) == C.CPATTN_EINVAL
+    assert _step(_dims(), ptrs=[ALIGNED + 2] + [ALIGNED] * 4) == C.CPATTN_EALIGN
+    assert _step(_dims(), scale=float("nan")) == C.CPATTN_EINVAL
+    assert C.lib().cpattn_step_fwd(None, 0, 0.0, 0, *([ALIGNED] * 5), 0) == C.CPATTN_EINVAL
+
+
+def test_partition_validation_before_launch():
+    L = C.lib()
+    d = _dims()
+    rope_bad = C.cpattn_rope(0.0)
+    assert L.cpattn_partition(ctypes.byref(_dims(s=510)), 0, 4, ALIGNED, ALIGNED, None, None,
+                              0) == C.CPATTN_ESHAPE
+    assert L.cpattn_partition(ctypes.byref(d), 5, 4, ALIGNED, ALIGNED, None, None,
+                              0) == C.CPATTN_EDTYPE
+    assert L.cpattn_partition(ctypes.byref(d), 0, 4, None, ALIGNED, None, None,
+                              0) == C.CPATTN_EINVAL
+    assert L.cpattn_partition(ctypes.byref(d), 0, 4, ALIGNED + 8, ALIGNED, None, None,
+                              0) == C.CPATTN_EALIGN
+    assert L.cpattn_partition(ctypes.byref(d), 0, 0, ALIGNED, ALIGNED, None, None,
+                              0) == C.CPATTN_ESHAPE
+    assert L.cpattn_partition(ctypes.byref(d), 0, 4, ALIGNED, ALIGNED, None,
+                              ctypes.byref(rope_bad), 0) == C.CPATTN_EINVAL
+
+
+def test_merge_validation_before_launch():
+    L = C.lib()
+    d = _dims()
+    two_c = 512 // 2
+    good = (C.cpattn_partial * 2)(C.cpattn_partial(ALIGNED, ALIGNED, 0, two_c),
+                                  C.cpattn_partial(ALIGNED, ALIGNED, 128, 128))
+    bad_rows = (C.cpattn_partial * 1)(C.cpattn_partial(ALIGNED, ALIGNED, 200, 100))
+    assert L.cpattn_merge(ctypes.byref(d), 0, good, 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
+    assert L.cpattn_merge(ctypes.byref(d), 65, good, 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
+    assert L.cpattn_merge(ctypes.byref(d), 1, bad_rows, 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
+    assert L.cpattn_merge(ctypes.byref(d), 2, good, 9, ALIGNED, None, 0) == C.CPATTN_EDTYPE
+    assert L.cpattn_merge(ctypes.byref(d), 2, good, 0, None, None, 0) == C.CPATTN_EINVAL
+    assert L.cpattn_merge(ctypes.byref(d), 2, good, 0, ALIGNED + 4, None, 0) == C.CPATTN_EALIGN
+    assert L.cpattn_merge(ctypes.byref(_dims(hq=256, hkv=4)), 64,
+                          (C.cpattn_partial * 64)(), 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
+
+
+def test_forward_workspace_and_validation():
+    L = C.lib()
+    d = _dims(b=1, s=32768, hq=64, hkv=8, d=128, cp=8)
+    ws = C.cpattn_forward_workspace(d, 3)
+    c = 32768 // 16
+    # 4 steps of 2c rows (causal + 3 kv_first_half) and 4 of c rows
+    want = 4 * (2 * c * 64 * 128 * 4 + 64 * 2 * c * 4) + 4 * (c * 64 * 128 * 4 + 64 * c * 4)
+    assert ws == want
+    assert C.cpattn_forward_workspace(d, 8) == 0
+    args = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), 3, ALIGNED, ALIGNED, ALIGNED,
+            ALIGNED, ws - 1, C.CPATTN_F32, ALIGNED, None, 0]
+    assert L.cpattn_forward(*args) == C.CPATTN_ENOSPACE
+    args[8] = ws
+    args[7] = ALIGNED + 16                         # workspace must be 256-aligned
+    assert L.cpattn_forward(*args) == C.CPATTN_EALIGN
+    args[7] = ALIGNED
+    args[3] = 8
+    assert L.cpattn_forward(*args) == C.CPATTN_EINVAL
+
+
+def test_binding_names_match_header():
+    for name in _declared_functions():
+        assert hasattr(C, name), name

@@ -1,0 +1,112 @@
+"""GPU end-to-end CP forward vs the non-CP oracle, per workload.
+
+* every workload at a reduced length (same heads, head dim, cp, dtype and
+  distribution; ragged tiles): every rank, every row, every head;
+* the fp32 workload at its full size, every rank and row (1e-5);
+* every bf16 workload at its full size, through the same calls the
+  benchmark times: sampled rows (chunk edges plus random rows) of every
+  rank (the RoPE workload: its measured rank) vs the oracle row by row.
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import (BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, C, CPProblem, assert_close,
+                         make_inputs, ocp, oracle_full, oracle_sampled_rows, run_rank,
+                         sample_local_rows, say, small, torch)
+from long_context_causal_amd.inputs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = [("fp32_mha_s512_cp2", 2 * 2 * 77, None),
+           ("bf16_gqa_s8k_cp4", 2 * 4 * 100, None),
+           ("bf16_gqa_s32k_cp8", 2 * 8 * 40, None),
+           ("bf16_mha_s16k_cp4_widelogits", 2 * 4 * 96, None),
+           ("bf16_gqa_s128k_cp16_rope", 2 * 16 * 24, None),
+           ("bf16_gqa_s8k_cp4", 2 * 4 * 256, 3)]
+
+
+def _bounds(w):
+    return (F32_MAX_ABS, None) if w.dtype == "f32" else (BF16_MAX_ABS, BF16_MEAN_ABS)
+
+
+@pytest.mark.parametrize("name,s,b", REDUCED)
+def test_forward_reduced_all_ranks(name, s, b):
+    w = small(WORKLOADS[name], s, b)
+    say(f"forward reduced {name} s={s} b={w.b}")
+    q, k, v = make_inputs(w)
+    o_full, l_full = oracle_full(w, q, k, v)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    mx_abs, mn_abs = _bounds(w)
+    for r in range(w.cp):
+        o, l = run_rank(P, r)
+        pos = ocp.zigzag_positions(w.s, w.cp, r)
+        assert_close(f"rank {r} O", o, o_full[:, pos], mx_abs, mn_abs)
+        assert_close(f"rank {r} L", l, l_full[:, :, pos], 1e-3 if w.dtype == "bf16" else 1e-5)
+
+
+def test_forward_fp32_full_size():
+    w = WORKLOADS["fp32_mha_s512_cp2"]
+    say(f"forward full {w.name}")
+    q, k, v = make_inputs(w)
+    o_full, l_full = oracle_full(w, q, k, v)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    for r in range(w.cp):
+        o, l = run_rank(P, r)
+        pos = ocp.zigzag_positions(w.s, w.cp, r)
+        assert_close(f"rank {r} O", o, o_full[:, pos], F32_MAX_ABS)
+        assert_close(f"rank {r} L", l, l_full[:, :, pos], F32_MAX_ABS)
+
+
+def test_stepwise_calls_equal_forward_entry_point():
+    """The benchmark's per-step calls and cpattn_forward give the same bits."""
+    w = small(WORKLOADS["bf16_gqa_s32k_cp8"], 2 * 8 * 64)
+    say("stepwise vs cpattn_forward")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    r = w.rank
+    a = P.alloc_rank(r)
+    for i in range(w.cp):
+        P.step(a, i)
+    P.merge(a)
+    b = P.alloc_rank(r)
+    P.forward(b)
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+
+
+FULL = [("bf16_gqa_s8k_cp4", 12), ("bf16_mha_s16k_cp4_widelogits", 8),
+        ("bf16_gqa_s32k_cp8", 6), ("bf16_gqa_s128k_cp16_rope", 24)]
+
+
+@pytest.mark.parametrize("name,n_mid", FULL)
+def test_forward_full_size_sampled_rows(name, n_mid):
+    w = WORKLOADS[name]
+    say(f"forward full {name}: inputs")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    ranks = [w.rank] if w.rope_theta is not None else list(range(w.cp))
+    out_dtype = C.CPATTN_BF16 if w.dtype == "bf16" else C.CPATTN_F32
+    errs = []
+    for r in ranks:
+        say(f"  rank {r}: gpu")
+        o, l = run_rank(P, r, C.CPATTN_F32)
+        rows = sample_local_rows(w.c, n_mid, seed=100 + r)
+        pos = ocp.zigzag_positions(w.s, w.cp, r)[rows]
+        say(f"  rank {r}: oracle on {len(rows)} rows")
+        o_ref, l_ref = oracle_sampled_rows(w, q, k, v, pos)
+        assert_close(f"rank {r} O", o[:, rows], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+        assert_close(f"rank {r} L", l[:, :, rows], l_ref, 1e-3)
+        errs.append(np.abs(o[:, rows] - o_ref).max())
+    say(f"  worst max abs over ranks {max(errs):.3e}")
+    # the bf16 output option: within one bf16 rounding of the fp32 output
+    r = ranks[0]
+    buf = P.alloc_rank(r, out_dtype)
+    P.forward(buf)
+    o32, _ = run_rank(P, r, C.CPATTN_F32)
+    from gpu_helpers import host_f32
+    ob = host_f32(buf["o"])
+    assert np.all(np.abs(ob - o32) <= np.abs(o32) * 2.0 ** -8 + 1e-30)

@@ -201,7 +201,19 @@ struct Kernel {
         issue(p, nK, nV, kbase, vbase, kstride, (t + NS - 1) * BN, wave, lane);
         const int key0 = t * BN;
         if (CAUSAL && key0 > wrow0 + 31) return;      // tile after every row of the wave
-        const bool need_mask = (key0 + BN > p.nk) || (CAUSAL && key0 + BN - 1 > wrow0);
+        // scalar branch: only tiles crossing the diagonal or the end mask
+        if ((key0 + BN > p.nk) || (CAUSAL && key0 + BN - 1 > wrow0))
+            compute<true>(p, S, sK, sV, key0, wrow0, lane);
+        else
+            compute<false>(p, S, sK, sV, key0, wrow0, lane);
+    }
+
+    // S^T = K Q^T, online softmax and O^T += V^T P^T for one resident tile.
+    template <bool MASK>
+    __device__ __forceinline__ static void compute(const Params &p, State &S, unsigned sK,
+                                                   unsigned sV, int key0, int wrow0, int lane) {
+        const int hi = lane >> 5;
+        const int l32 = lane & 31;
 
         // S^T = K Q^T over the 64-key tile: two 32-key halves
         f32x16 s[2];
@@ -232,7 +244,7 @@ struct Kernel {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float x = s[h2][e];
-                if (need_mask) {
+                if constexpr (MASK) {
                     const int key = key0 + h2 * 32 + 16 * (e >> 3) + 8 * hi + (e & 7);
                     const bool vis = key < p.nk && (!CAUSAL || key <= qrow);
                     x = vis ? x : -INFINITY;
@@ -251,22 +263,25 @@ struct Kernel {
         }
         const float mu = (S.m_run == -INFINITY) ? 0.0f : S.m_run;
         bf16x8 pf[BN / 16];
-        float lsum = 0.0f;
+        float lsum0 = 0.0f, lsum1 = 0.0f;   // two partial row sums (shorter chains)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 f32x8 pv;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(
+                for (int e = 0; e < 8; ++e)
+                    pv[e] = __builtin_amdgcn_exp2f(
                         __builtin_fmaf(s[h2][half * 8 + e], p.scale_log2, -mu));
-                    pv[e] = pe;
-                    lsum += pe;
+                const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
+                pf[h2 * 2 + half] = pb;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    lsum0 += pv[e];
+                    lsum1 += pv[e + 1];
                 }
-                pf[h2 * 2 + half] = __builtin_convertvector(pv, bf16x8);
             }
-        S.l_run += lsum;
+        S.l_run += lsum0 + lsum1;
 
         // O^T += V^T P^T; the V^T operand of each MFMA is two transposing reads
         unsigned av[4];
@@ -291,7 +306,9 @@ struct Kernel {
     __device__ __forceinline__ static void run(const Params &p, char *lds) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
-        const int wave = tid >> 6;
+        // wave index as a scalar: every per-wave decision below (mask, skip)
+        // is then a scalar branch instead of a per-lane select
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int hi = lane >> 5;
         const int l32 = lane & 31;
 

@@ -8,12 +8,19 @@
 // internal.h: q_row0, nq, nk, causal).
 //
 // Work decomposition
-//   workgroup = NW waves = BM = 32*NW query rows of one (batch, head); each
-//   wave owns 32 consecutive rows.  The KV block streams through LDS in
-//   tiles of BN = 64 keys held in a ring of NS stages.  Tiles are copied
-//   global -> LDS directly (global_load_lds_dwordx4, no VGPR round trip),
-//   NS-1 tiles ahead of the one being computed, so HBM/L2 latency hides
-//   behind NS-1 tiles of matrix work; one barrier per tile.
+//   workgroup = 8 waves = 256 query rows of one (batch, head); each wave
+//   owns 32 consecutive rows.  The KV block streams through LDS in tiles of
+//   BN = 64 keys held in a ring of 4 stages, copied global -> LDS directly
+//   (global_load_lds_dwordx4, no VGPR round trip) two tiles ahead.
+//
+// Schedule ("ping-pong"): a wave alternates a matrix phase G(t) = {S^T(t) =
+//   K(t) Q^T, O^T += V(t-1)^T P(t-1)} and a vector phase V(t) = {online
+//   softmax of S(t) into P(t)}.  Waves 4-7 run one phase behind waves 0-3,
+//   and one workgroup barrier separates phases, so on every SIMD (one wave
+//   of each group) one wave issues matrix instructions while the other
+//   issues the softmax: the exp/max/sum work hides under the MFMAs.  Inside
+//   a matrix phase the LDS reads of the next group of four MFMAs are in
+//   flight while the current four execute.
 //
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16; lane = 32*hi + l32)
 //   Scores are computed transposed, S^T = K Q^T (M = keys, N = queries,
@@ -39,6 +46,11 @@
 // LDS (64 banks x 4 bytes on gfx950): rows are 256 bytes; 16-byte chunks
 // are XOR-swizzled per row (K: by the matrix row feeding it, V: by key%4)
 // so every ds_read_b128 / ds_read_b64_tr_b16 phase hits distinct banks.
+// The global -> LDS copies are issued from inline assembly, so the compiler
+// does not track them (it would otherwise wait for every copy in flight
+// before each LDS read, as it cannot tell the stages apart); explicit vmcnt
+// waits before the barrier that publishes a tile complete them.  LDS reads
+// are ordinary loads and transposing-read builtins the compiler schedules.
 #include "internal.h"
 
 #include <math.h>
@@ -53,12 +65,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 128;
 constexpr int BN = 64;                 // keys per LDS tile
+constexpr int NW = 8;                  // waves per workgroup
+constexpr int BM = 32 * NW;            // query rows per workgroup
+constexpr int NS = 4;                  // LDS stages
 constexpr int ROWB = D * 2;            // bytes per K/V row in LDS
 constexpr int TILEB = BN * ROWB;       // bytes per K (or V) tile
+constexpr int KI = BN / 4 / NW;        // copy instructions per wave per tile (each)
+constexpr int LPT = 2 * KI;            // copies per wave per tile (K and V)
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units a stale max may lag
 
 struct Params {
@@ -81,77 +97,41 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// The tile reads are issued from inline assembly: the compiler cannot tell
-// the LDS stages apart from the in-flight global->LDS copies and would
-// otherwise wait for every copy before each read.  Each block ends with
-// lgkmcnt(0), so its outputs are complete when it returns.
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-// K operands (A of S^T = K Q^T) for k-steps kk0..kk0+3 and both 32-key
-// halves of the tile: a[kk] addresses the lane's 16-byte chunk of k-step kk
-// in the first half; the second half is 32 rows (8 KiB) further.
-__device__ __forceinline__ void read_k4(const unsigned (&a)[4], bf16x8 (&kf)[4][2]) {
-    u32x4 r[8];
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:8192\n\t"
-        "ds_read_b128 %2, %9\n\t"
-        "ds_read_b128 %3, %9 offset:8192\n\t"
-        "ds_read_b128 %4, %10\n\t"
-        "ds_read_b128 %5, %10 offset:8192\n\t"
-        "ds_read_b128 %6, %11\n\t"
-        "ds_read_b128 %7, %11 offset:8192\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-          "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        kf[i][0] = __builtin_bit_cast(bf16x8, r[2 * i]);
-        kf[i][1] = __builtin_bit_cast(bf16x8, r[2 * i + 1]);
-    }
+// K operand of one k-step for one 32-key half: the lane's 16-byte chunk.
+__device__ __forceinline__ bf16x8 k_read(unsigned addr) {
+    return __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)(uintptr_t)addr);
 }
 
-// V^T operands of key chunk kc (16 keys) for the four 32-wide head-dim
-// tiles.  Lane L = 16*g + 4*j + q reads, for s in {0, 1}, the 8-byte block at
-// V row kc*16 + 8*(g/2) + 4*s + j, head dims dt*32 + 16*(g%2) + 4*q .. +3;
-// the transpose hands lane t of group g the column dt*32 + 16*(g%2) + t for
-// keys +0..3 of that row block.  a[dt] addresses row 8*(g/2) + j of dims
-// tile dt (rows kc*16 and +4 are immediate offsets).
-template <int KC>
-__device__ __forceinline__ void read_vt(const unsigned (&a)[4], bf16x8 (&vf)[4]) {
-    s16x4 r[8];
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
-        "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-          "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(KC * 16 * ROWB),
-          "i"(KC * 16 * ROWB + 4 * ROWB));
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-        vf[dt] = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(r[2 * dt], r[2 * dt + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+// V^T operand of key chunk kc (16 keys) for one 32-wide head-dim tile.  Lane
+// L = 16*g + 4*j + q reads, for s in {0, 1}, the 8-byte block at V row
+// kc*16 + 8*(g/2) + 4*s + j, head dims dt*32 + 16*(g%2) + 4*q .. +3; the
+// transpose hands lane t of group g the column dt*32 + 16*(g%2) + t for keys
+// +0..3 of that row block.  addr: row 8*(g/2) + j of the tile's dims block.
+__device__ __forceinline__ bf16x8 vt_read(unsigned addr) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)addr);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)(uintptr_t)(addr + 4 * ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int NW, int NS, bool CAUSAL>
+// One direct global -> LDS copy of 16 bytes per lane; lane L writes
+// lds_base + 16*L.  m0 carries the (wave-uniform) LDS base.
+__device__ __forceinline__ void dma16(const void *src, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_base)
+                 : "memory");
+}
+
+template <bool CAUSAL>
 struct Kernel {
-    static constexpr int BM = 32 * NW;
-    static constexpr int NT = 64 * NW;
-    // global->LDS instructions per wave per tile (K and V each)
-    static constexpr int KI = BN / 4 / NW;    // one instruction fills 4 rows
-    static constexpr int LOADS_PER_TILE = 2 * KI;
-    static_assert(KI >= 1, "need at most 16 waves");
-
     // Issue this wave's share of the direct copies of tile `key0` into one
-    // LDS stage (sK, sV).
-    __device__ __forceinline__ static void issue(const Params &p, char *sK, char *sV,
+    // LDS stage (K at sK, V at sK + TILEB).  Rows past the block are clamped
+    // to its last row.
+    __device__ __forceinline__ static void issue(const Params &p, unsigned sK,
                                                  const uint16_t *kbase, const uint16_t *vbase,
                                                  int64_t kstride, int key0, int wave, int lane) {
 #pragma unroll
@@ -162,96 +142,93 @@ struct Kernel {
             const int kchunk = phys ^ (swap_bits23(row) & 15);
             const int vchunk = phys ^ ((row & 3) << 2);
             const int64_t goff = (int64_t)key * kstride;
-            char *kdst = sK + (wave * KI + i) * 4 * ROWB;
-            char *vdst = sV + (wave * KI + i) * 4 * ROWB;
-            __builtin_amdgcn_global_load_lds((const void *)(kbase + goff + kchunk * 8),
-                                             (lds_void *)kdst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(vbase + goff + vchunk * 8),
-                                             (lds_void *)vdst, 16, 0, 0);
+            const unsigned dst = sK + (wave * KI + i) * 4 * ROWB;
+            dma16(kbase + goff + kchunk * 8, dst);
+            dma16(vbase + goff + vchunk * 8, dst + TILEB);
         }
     }
 
-    // Per-wave state carried from tile to tile.
+    // Per-wave state.
     struct State {
-        bf16x8 qf[D / 16];
-        f32x16 acc[D / 32];
+        bf16x8 qf[D / 16];       // Q as the B operand of S^T
+        f32x16 acc[D / 32];      // O^T
+        f32x16 s[2];             // S^T of the tile between its two phases
+        bf16x8 pf[BN / 16];      // P of the tile between its two phases
         float m_run, l_run;
         unsigned koff[D / 16];   // lane's byte offset of each K chunk in a stage
         unsigned voff[D / 32];   // lane's byte offset of each V^T read in a stage
     };
 
-    // One KV tile: wait for its copies, barrier, refill the stage freed by
-    // the previous tile, then S^T = K Q^T, online softmax, O^T += V^T P^T.
-    __device__ __forceinline__ static void tile(const Params &p, State &S, int t, int ntiles,
-                                                unsigned sK, unsigned sV, char *nK,
-                                                char *nV, const uint16_t *kbase,
-                                                const uint16_t *vbase, int64_t kstride,
-                                                int wrow0, int wave, int lane) {
-        const int hi = lane >> 5;
-        const int l32 = lane & 31;
-        // Own copies of tile t done (the NS-2 tiles issued after it may still
-        // be in flight), then all waves' copies: barrier.  The barrier also
-        // retires every wave's reads of the stage refilled below (they fed
-        // tile t-1's MFMAs).  Copies are issued for every tile index, also
-        // past the end (rows clamped, never read), so the number in flight is
-        // the same at every wait.
-        wait_vmcnt<LOADS_PER_TILE * (NS - 2)>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        asm volatile("s_barrier" ::: "memory");
-        issue(p, nK, nV, kbase, vbase, kstride, (t + NS - 1) * BN, wave, lane);
-        const int key0 = t * BN;
-        if (CAUSAL && key0 > wrow0 + 31) return;      // tile after every row of the wave
-        // scalar branch: only tiles crossing the diagonal or the end mask
-        if ((key0 + BN > p.nk) || (CAUSAL && key0 + BN - 1 > wrow0))
-            compute<true>(p, S, sK, sV, key0, wrow0, lane);
-        else
-            compute<false>(p, S, sK, sV, key0, wrow0, lane);
+    // Matrix phase: S^T(t) = K(t) Q^T and O^T += V(t-1)^T P(t-1).  sK: stage
+    // of tile t, sV: V tile of tile t-1.  One code path for every phase: the
+    // first phase multiplies a zeroed V tile by P = 0, and the S^T of the
+    // phase after a wave's last tile is computed on resident rows and dropped.
+    __device__ __forceinline__ static void matrix_phase(State &S, unsigned sK, unsigned sV) {
+        // Eight steps of four MFMAs: step i does k-step i of S^T (both 32-key
+        // halves) and head-dim tiles 2(i%2), 2(i%2)+1 of key chunk i/2 of O^T.
+        // The LDS reads of step i+2 are issued before the MFMAs of step i, so
+        // two steps of matrix work cover each read's latency (the fences keep
+        // the compiler from hoisting every read, which would exhaust registers).
+        bf16x8 kf[3][2], vf[3][2];
+        auto reads = [&](int i, int slot) {
+            kf[slot][0] = k_read(sK + S.koff[i]);
+            kf[slot][1] = k_read(sK + S.koff[i] + 32 * ROWB);
+            const int kc = i >> 1, dt0 = 2 * (i & 1);
+            vf[slot][0] = vt_read(sV + S.voff[dt0] + kc * 16 * ROWB);
+            vf[slot][1] = vt_read(sV + S.voff[dt0 + 1] + kc * 16 * ROWB);
+        };
+        reads(0, 0);
+        reads(1, 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int cur = i % 3;
+            if (i + 2 < 8) reads(i + 2, (i + 2) % 3);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                S.s[h2] = i == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                       kf[cur][h2], S.qf[i], f32x16{}, 0, 0, 0)
+                                 : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                       kf[cur][h2], S.qf[i], S.s[h2], 0, 0, 0);
+            const int kc = i >> 1, dt0 = 2 * (i & 1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                S.acc[dt0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][j], S.pf[kc],
+                                                                         S.acc[dt0 + j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
-    // S^T = K Q^T, online softmax and O^T += V^T P^T for one resident tile.
+    // Row max of the tile's raw scores; the masked variant first sets the
+    // invisible scores to -inf (keys past the block, or after the row).
     template <bool MASK>
-    __device__ __forceinline__ static void compute(const Params &p, State &S, unsigned sK,
-                                                   unsigned sV, int key0, int wrow0, int lane) {
-        const int hi = lane >> 5;
-        const int l32 = lane & 31;
-
-        // S^T = K Q^T over the 64-key tile: two 32-key halves
-        f32x16 s[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[h2][e] = 0.0f;
-#pragma unroll
-        for (int k4 = 0; k4 < D / 64; ++k4) {
-            unsigned a[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = sK + S.koff[k4 * 4 + i];
-            bf16x8 kf[4][2];
-            read_k4(a, kf);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-                    s[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i][h2], S.qf[k4 * 4 + i],
-                                                                   s[h2], 0, 0, 0);
-        }
-
-        // online softmax in the log2 domain
-        const int qrow = wrow0 + l32;
+    __device__ __forceinline__ static float tile_max(const Params &p, State &S, int key0,
+                                                     int qrow, int hi) {
         float tmax = -INFINITY;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                float x = s[h2][e];
+                float x = S.s[h2][e];
                 if constexpr (MASK) {
                     const int key = key0 + h2 * 32 + 16 * (e >> 3) + 8 * hi + (e & 7);
                     const bool vis = key < p.nk && (!CAUSAL || key <= qrow);
                     x = vis ? x : -INFINITY;
-                    s[h2][e] = x;
+                    S.s[h2][e] = x;
                 }
                 tmax = fmaxf(tmax, x);
             }
+        return tmax;
+    }
+
+    // Vector phase: online softmax of S(t) into P(t), rescaling O and l
+    // first when the running max moves by more than the slack.
+    __device__ __forceinline__ static void softmax_phase(const Params &p, State &S, int key0,
+                                                         bool mask, int wrow0, int lane) {
+        const int hi = lane >> 5;
+        const int qrow = wrow0 + (lane & 31);
+        float tmax = mask ? tile_max<true>(p, S, key0, qrow, hi)
+                          : tile_max<false>(p, S, key0, qrow, hi);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
         const float m_new = fmaxf(S.m_run, tmax);
         if (__builtin_amdgcn_ballot_w64(m_new > S.m_run + RESCALE_SLACK)) {
@@ -262,7 +239,6 @@ struct Kernel {
             S.m_run = m_new;
         }
         const float mu = (S.m_run == -INFINITY) ? 0.0f : S.m_run;
-        bf16x8 pf[BN / 16];
         float lsum0 = 0.0f, lsum1 = 0.0f;   // two partial row sums (shorter chains)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
@@ -272,43 +248,40 @@ struct Kernel {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     pv[e] = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(s[h2][half * 8 + e], p.scale_log2, -mu));
-                const bf16x8 pb = __builtin_convertvector(pv, bf16x8);
-                pf[h2 * 2 + half] = pb;
+                        __builtin_fmaf(S.s[h2][half * 8 + e], p.scale_log2, -mu));
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
                     lsum0 += pv[e];
                     lsum1 += pv[e + 1];
                 }
+                S.pf[h2 * 2 + half] = __builtin_convertvector(pv, bf16x8);
             }
         S.l_run += lsum0 + lsum1;
-
-        // O^T += V^T P^T; the V^T operand of each MFMA is two transposing reads
-        unsigned av[4];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) av[dt] = sV + S.voff[dt];
-        pv_chunk<0>(S, av, pf[0]);
-        pv_chunk<1>(S, av, pf[1]);
-        pv_chunk<2>(S, av, pf[2]);
-        pv_chunk<3>(S, av, pf[3]);
     }
 
-    template <int KC>
-    __device__ __forceinline__ static void pv_chunk(State &S, const unsigned (&av)[4],
-                                                    const bf16x8 &pfk) {
-        bf16x8 vf[4];
-        read_vt<KC>(av, vf);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-            S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[dt], pfk, S.acc[dt], 0, 0, 0);
+    // The barrier opening half-iteration h.  At even h = 2u: this wave's
+    // copies of tile u are complete before it (the copies of tile u+1 may
+    // still fly), and the copies of tile u+2 are issued after it.
+    __device__ __forceinline__ static void sync(const Params &p, State &S, int h,
+                                                unsigned lds_addr, const uint16_t *kbase,
+                                                const uint16_t *vbase, int64_t kstride, int wave,
+                                                int lane) {
+        const bool even = (h & 1) == 0;
+        if (even) wait_vmcnt<LPT>();
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (even) {
+            const int u = (h >> 1) + 2;
+            issue(p, lds_addr + (u % NS) * 2 * TILEB, kbase, vbase, kstride, u * BN, wave, lane);
+        }
     }
 
     __device__ __forceinline__ static void run(const Params &p, char *lds) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
-        // wave index as a scalar: every per-wave decision below (mask, skip)
-        // is then a scalar branch instead of a per-lane select
+        // wave index as a scalar: every per-wave decision below is a scalar
+        // branch instead of a per-lane select
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int grp = wave >> 2;                   // 0: leading, 1: trailing group
         const int hi = lane >> 5;
         const int l32 = lane & 31;
 
@@ -331,35 +304,31 @@ struct Kernel {
 
         const int kend = CAUSAL ? min(p.nk, qtile * BM + BM) : p.nk;
         const int ntiles = (kend + BN - 1) / BN;
+        // tiles this wave computes: causal waves stop at their diagonal
+        const int tl = CAUSAL ? min(ntiles, (wrow0 + 31) / BN + 1) : ntiles;
         const uint16_t *kbase = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
         const uint16_t *vbase = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
         const int64_t kstride = (int64_t)p.hkv * D;
 
         State S;
-        // Q fragments (B operand of S^T): lane holds query l32, dims kk*16+8*hi..
-        {
-            const int row = min(wrow0 + l32, p.nq - 1);
-            const uint16_t *src =
-                p.q + ((n * p.two_c + p.q_row0 + row) * (int64_t)p.hq + head) * D + hi * 8;
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-                S.qf[kk] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + kk * 16));
-        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) S.acc[dt][e] = 0.0f;
         S.m_run = -INFINITY;
         S.l_run = 0.0f;
-
-        // prologue: the first NS-1 tiles in flight (after the Q loads, so the
-        // in-order vector-memory counter retires Q first)
 #pragma unroll
-        for (int s = 0; s < NS - 1; ++s)
-            issue(p, lds + s * 2 * TILEB, lds + s * 2 * TILEB + TILEB, kbase, vbase, kstride,
-                  s * BN, wave, lane);
+        for (int kc = 0; kc < BN / 16; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) S.pf[kc][e] = (__bf16)0.0f;
+        // the V tile the first matrix phase reads (stage NS-1) starts as zeros;
+        // its first copy is issued two barriers later
+        {
+            u32x4 *z = (u32x4 *)(lds + (NS - 1) * 2 * TILEB + TILEB);
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            for (int i = tid; i < TILEB / 16; i += 64 * NW) z[i] = zero;
+        }
 
-        // lane byte offsets of the tile reads inside a stage (see read_k4/read_vt)
         {
             const int krow = swap_bits23(l32);             // K row fed to matrix row l32
 #pragma unroll
@@ -374,23 +343,46 @@ struct Kernel {
         }
         const unsigned lds_addr =
             (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
-        // Q has landed once only the prologue copies are outstanding
-        wait_vmcnt<LOADS_PER_TILE * (NS - 1)>();
-
-        // the ring, unrolled by stage so stage offsets are constants
-        for (int t0 = 0; t0 < ntiles; t0 += NS) {
+        // prologue: tiles 0 and 1 in flight, then Q; one full wait before the
+        // loop (tile 0 has to land first anyway) also tells the compiler that
+        // Q is resident, so it puts no memory wait inside the loop
+        issue(p, lds_addr, kbase, vbase, kstride, 0, wave, lane);
+        issue(p, lds_addr + 2 * TILEB, kbase, vbase, kstride, BN, wave, lane);
+        {
+            const int row = min(wrow0 + l32, p.nq - 1);
+            const uint16_t *src =
+                p.q + ((n * p.two_c + p.q_row0 + row) * (int64_t)p.hq + head) * D + hi * 8;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if (t0 + s < ntiles) {
-                    const int nxt = (s + NS - 1) % NS;
-                    tile(p, S, t0 + s, ntiles, lds_addr + s * 2 * TILEB,
-                         lds_addr + s * 2 * TILEB + TILEB, lds + nxt * 2 * TILEB,
-                         lds + nxt * 2 * TILEB + TILEB, kbase, vbase, kstride, wrow0, wave, lane);
-                }
+            for (int kk = 0; kk < D / 16; ++kk)
+                S.qf[kk] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + kk * 16));
+        }
+        wait_vmcnt<0>();
+
+        // Half-iterations h = 0 .. 2T+1, one barrier each.  The leading group
+        // runs phase h, the trailing group phase h-1: phase 2t is the matrix
+        // phase G(t), phase 2t+1 the softmax of tile t.  At even h = 2u tile u
+        // must be resident (its K is read now, its V two phases later) and
+        // tile u+2 is copied into the stage tile u-2 left (its last reader ran
+        // at h-1).  The trailing group's first and the leading group's last
+        // half-iteration are idle.
+        if (grp == 1) sync(p, S, 0, lds_addr, kbase, vbase, kstride, wave, lane);
+        for (int t = 0; t <= ntiles; ++t) {
+            const int hg = 2 * t + grp;
+            sync(p, S, hg, lds_addr, kbase, vbase, kstride, wave, lane);
+            if (t <= tl)
+                matrix_phase(S, lds_addr + (t % NS) * 2 * TILEB,
+                             lds_addr + ((t + NS - 1) % NS) * 2 * TILEB + TILEB);
+            if (t == ntiles) break;
+            sync(p, S, hg + 1, lds_addr, kbase, vbase, kstride, wave, lane);
+            if (t < tl) {
+                const int key0 = t * BN;
+                // scalar: only tiles crossing the diagonal or the block end mask
+                const bool mask = (key0 + BN > p.nk) || (CAUSAL && key0 + BN - 1 > wrow0);
+                softmax_phase(p, S, key0, mask, wrow0, lane);
             }
         }
-
-        // the copies past the end land in stages nobody reads; retire them
+        if (grp == 0) sync(p, S, 2 * ntiles + 1, lds_addr, kbase, vbase, kstride, wave, lane);
+        // copies issued past the end land in stages nobody reads; retire them
         // before the workgroup's LDS is handed to the next workgroup
         wait_vmcnt<0>();
 
@@ -416,17 +408,16 @@ struct Kernel {
     }
 };
 
-template <int NW, int NS, bool CAUSAL>
-__global__ void __launch_bounds__(64 * NW) attn_step_bf16(Params p) {
-    // NS stages of (K tile, V tile)
+template <bool CAUSAL>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_step_bf16(Params p) {
     __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
-    Kernel<NW, NS, CAUSAL>::run(p, lds);
+    Kernel<CAUSAL>::run(p, lds);
 }
 
-template <int NW, int NS, bool CAUSAL>
+template <bool CAUSAL>
 hipError_t launch(const StepGeom &g, const void *q, const void *k, const void *v, float *o,
                   float *lse, hipStream_t stream) {
-    constexpr int BM = 32 * NW;
     Params p;
     p.q = (const uint16_t *)q;
     p.k = (const uint16_t *)k;
@@ -443,20 +434,17 @@ hipError_t launch(const StepGeom &g, const void *q, const void *k, const void *v
     p.num_qtiles = (int)((g.nq + BM - 1) / BM);
     p.scale_log2 = g.scale_log2;
     const int64_t blocks = (int64_t)p.num_qtiles * g.hq * g.b;
-    hipLaunchKernelGGL((attn_step_bf16<NW, NS, CAUSAL>), dim3((unsigned)blocks), dim3(64 * NW),
-                       0, stream, p);
+    hipLaunchKernelGGL((attn_step_bf16<CAUSAL>), dim3((unsigned)blocks), dim3(64 * NW), 0,
+                       stream, p);
     return hipGetLastError();
 }
-
-constexpr int kWaves = 8;
-constexpr int kStages = 3;
 
 }  // namespace
 
 hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, const void *v,
                             float *o, float *lse, hipStream_t stream) {
-    if (g.causal) return launch<kWaves, kStages, true>(g, q, k, v, o, lse, stream);
-    return launch<kWaves, kStages, false>(g, q, k, v, o, lse, stream);
+    if (g.causal) return launch<true>(g, q, k, v, o, lse, stream);
+    return launch<false>(g, q, k, v, o, lse, stream);
 }
 
 }  // namespace cpattn

@@ -39,6 +39,30 @@ def parse():
     return ap.parse_args()
 
 
+def committed_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary.
+
+    The summary records the sha256 of the kernel source it was measured
+    with; if the source has changed since, the figure no longer describes
+    this kernel and None is returned.
+    """
+    import hashlib
+    src = os.path.join(ROOT, "long_context_causal_amd", "csrc", "attn_step_bf16.hip")
+    prof = os.path.join(ROOT, "profiles", f"attn_step_bf16__{workload}__hbm_traffic.txt")
+    if not os.path.exists(prof):
+        return None
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    recorded, traffic = None, None
+    with open(prof) as f:
+        for line in f:
+            if "kernel source sha256" in line:
+                recorded = line.rsplit(":", 1)[1].strip()
+            if line.startswith("attention_traffic_bytes_per_launch:"):
+                traffic = float(line.split(":", 1)[1])
+    return traffic if recorded == digest else None
+
+
 def cpu_baseline(w, q, k, v, rank, target_s):
     """Oracle (fp64, OpenMP) on every stride-th local row of the rank share."""
     import numpy as np
@@ -166,8 +190,11 @@ def main():
                    "d": w.d, "cp": w.cp, "rank": rank,
                    "rope_theta": w.rope_theta},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": None,
-                     "kernel": "attn_step_bf16" if w.dtype == "bf16" else "attn_step_f32"},
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": committed_traffic(w.name) if w.dtype == "bf16" else None,
+                     "kernel": "attn_step_bf16" if w.dtype == "bf16" else "attn_step_f32",
+                     "flops_per_launch": flops / w.cp,
+                     "avg_launch_ms": round(attn_ms / w.cp, 4)},
         "pct_of_peak": round(100 * value / peak, 2),
         "kernels_ms": {"partition_qkv": round(mean(part_ms), 4),
                        "steps": [round(x, 4) for x in steps_ms],

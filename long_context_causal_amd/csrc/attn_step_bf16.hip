@@ -49,8 +49,11 @@
 // The global -> LDS copies are issued from inline assembly, so the compiler
 // does not track them (it would otherwise wait for every copy in flight
 // before each LDS read, as it cannot tell the stages apart); explicit vmcnt
-// waits before the barrier that publishes a tile complete them.  LDS reads
-// are ordinary loads and transposing-read builtins the compiler schedules.
+// waits before the barrier that publishes a tile complete them.  Each copy
+// takes the tile's base address in SGPRs and a per-lane byte offset fixed
+// for the whole kernel, so issuing a tile costs no vector address math.
+// LDS reads are ordinary loads and transposing-read builtins the compiler
+// schedules.
 #include "internal.h"
 
 #include <math.h>
@@ -117,37 +120,19 @@ __device__ __forceinline__ bf16x8 vt_read(unsigned addr) {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// One direct global -> LDS copy of 16 bytes per lane; lane L writes
-// lds_base + 16*L.  m0 carries the (wave-uniform) LDS base.
-__device__ __forceinline__ void dma16(const void *src, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+// One direct global -> LDS copy of 16 bytes per lane from base + off (base
+// wave-uniform, in SGPRs; off a per-lane byte offset); lane L writes
+// lds_base + 16*L.  m0 carries the LDS base; one wait state separates its
+// write from the copy that reads it.
+__device__ __forceinline__ void dma16(const void *base, unsigned off, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(src), "s"(lds_base)
+                 : "v"(off), "s"(base), "s"(lds_base)
                  : "memory");
 }
 
 template <bool CAUSAL>
 struct Kernel {
-    // Issue this wave's share of the direct copies of tile `key0` into one
-    // LDS stage (K at sK, V at sK + TILEB).  Rows past the block are clamped
-    // to its last row.
-    __device__ __forceinline__ static void issue(const Params &p, unsigned sK,
-                                                 const uint16_t *kbase, const uint16_t *vbase,
-                                                 int64_t kstride, int key0, int wave, int lane) {
-#pragma unroll
-        for (int i = 0; i < KI; ++i) {
-            const int row = (wave * KI + i) * 4 + (lane >> 4);
-            const int phys = lane & 15;
-            const int key = min(key0 + row, p.nk - 1);
-            const int kchunk = phys ^ (swap_bits23(row) & 15);
-            const int vchunk = phys ^ ((row & 3) << 2);
-            const int64_t goff = (int64_t)key * kstride;
-            const unsigned dst = sK + (wave * KI + i) * 4 * ROWB;
-            dma16(kbase + goff + kchunk * 8, dst);
-            dma16(vbase + goff + vchunk * 8, dst + TILEB);
-        }
-    }
-
     // Per-wave state.
     struct State {
         bf16x8 qf[D / 16];       // Q as the B operand of S^T
@@ -157,7 +142,42 @@ struct Kernel {
         float m_run, l_run;
         unsigned koff[D / 16];   // lane's byte offset of each K chunk in a stage
         unsigned voff[D / 32];   // lane's byte offset of each V^T read in a stage
+        unsigned gk[KI], gv[KI]; // lane's byte offsets of its K and V copies in a tile
+        int krow[KI];            // tile row of each of the lane's copies
+        const uint16_t *kbase, *vbase;
+        int64_t kstride;         // elements between consecutive keys
     };
+
+    // Issue this wave's share of the direct copies of tile `key0` into one
+    // LDS stage (K at sK, V at sK + TILEB): a scalar tile base plus the
+    // lane's fixed offsets.  A tile crossing the block end repeats row nk-1.
+    __device__ __forceinline__ static void issue(const Params &p, const State &S, unsigned sK,
+                                                 int key0, int wave) {
+        if (key0 + BN <= p.nk) {
+            const uint16_t *kb = S.kbase + (int64_t)key0 * S.kstride;
+            const uint16_t *vb = S.vbase + (int64_t)key0 * S.kstride;
+#pragma unroll
+            for (int i = 0; i < KI; ++i) {
+                const unsigned dst = sK + (wave * KI + i) * 4 * ROWB;
+                dma16(kb, S.gk[i], dst);
+                dma16(vb, S.gv[i], dst + TILEB);
+            }
+        } else {
+            // base row b0 <= every row copied, so lane offsets stay >= 0
+            const int b0 = max(min(key0, p.nk - BN), 0);
+            const uint16_t *kb = S.kbase + (int64_t)b0 * S.kstride;
+            const uint16_t *vb = S.vbase + (int64_t)b0 * S.kstride;
+#pragma unroll
+            for (int i = 0; i < KI; ++i) {
+                const int key = min(key0 + S.krow[i], p.nk - 1);
+                // gk holds krow rows; move the lane to row key - b0
+                const unsigned adj = (unsigned)((key - b0 - S.krow[i]) * (int)S.kstride * 2);
+                const unsigned dst = sK + (wave * KI + i) * 4 * ROWB;
+                dma16(kb, S.gk[i] + adj, dst);
+                dma16(vb, S.gv[i] + adj, dst + TILEB);
+            }
+        }
+    }
 
     // Matrix phase: S^T(t) = K(t) Q^T and O^T += V(t-1)^T P(t-1).  sK: stage
     // of tile t, sV: V tile of tile t-1.  One code path for every phase: the
@@ -263,15 +283,13 @@ struct Kernel {
     // copies of tile u are complete before it (the copies of tile u+1 may
     // still fly), and the copies of tile u+2 are issued after it.
     __device__ __forceinline__ static void sync(const Params &p, State &S, int h,
-                                                unsigned lds_addr, const uint16_t *kbase,
-                                                const uint16_t *vbase, int64_t kstride, int wave,
-                                                int lane) {
+                                                unsigned lds_addr, int wave) {
         const bool even = (h & 1) == 0;
         if (even) wait_vmcnt<LPT>();
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (even) {
             const int u = (h >> 1) + 2;
-            issue(p, lds_addr + (u % NS) * 2 * TILEB, kbase, vbase, kstride, u * BN, wave, lane);
+            issue(p, S, lds_addr + (u % NS) * 2 * TILEB, u * BN, wave);
         }
     }
 
@@ -306,11 +324,18 @@ struct Kernel {
         const int ntiles = (kend + BN - 1) / BN;
         // tiles this wave computes: causal waves stop at their diagonal
         const int tl = CAUSAL ? min(ntiles, (wrow0 + 31) / BN + 1) : ntiles;
-        const uint16_t *kbase = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
-        const uint16_t *vbase = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
-        const int64_t kstride = (int64_t)p.hkv * D;
-
         State S;
+        S.kbase = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
+        S.vbase = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
+        S.kstride = (int64_t)p.hkv * D;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+            const int row = (wave * KI + i) * 4 + (lane >> 4);
+            const int phys = lane & 15;
+            S.krow[i] = row;
+            S.gk[i] = (unsigned)(row * S.kstride * 2 + ((phys ^ (swap_bits23(row) & 15)) << 4));
+            S.gv[i] = (unsigned)(row * S.kstride * 2 + ((phys ^ ((row & 3) << 2)) << 4));
+        }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -346,8 +371,8 @@ struct Kernel {
         // prologue: tiles 0 and 1 in flight, then Q; one full wait before the
         // loop (tile 0 has to land first anyway) also tells the compiler that
         // Q is resident, so it puts no memory wait inside the loop
-        issue(p, lds_addr, kbase, vbase, kstride, 0, wave, lane);
-        issue(p, lds_addr + 2 * TILEB, kbase, vbase, kstride, BN, wave, lane);
+        issue(p, S, lds_addr, 0, wave);
+        issue(p, S, lds_addr + 2 * TILEB, BN, wave);
         {
             const int row = min(wrow0 + l32, p.nq - 1);
             const uint16_t *src =
@@ -365,15 +390,15 @@ struct Kernel {
         // tile u+2 is copied into the stage tile u-2 left (its last reader ran
         // at h-1).  The trailing group's first and the leading group's last
         // half-iteration are idle.
-        if (grp == 1) sync(p, S, 0, lds_addr, kbase, vbase, kstride, wave, lane);
+        if (grp == 1) sync(p, S, 0, lds_addr, wave);
         for (int t = 0; t <= ntiles; ++t) {
             const int hg = 2 * t + grp;
-            sync(p, S, hg, lds_addr, kbase, vbase, kstride, wave, lane);
+            sync(p, S, hg, lds_addr, wave);
             if (t <= tl)
                 matrix_phase(S, lds_addr + (t % NS) * 2 * TILEB,
                              lds_addr + ((t + NS - 1) % NS) * 2 * TILEB + TILEB);
             if (t == ntiles) break;
-            sync(p, S, hg + 1, lds_addr, kbase, vbase, kstride, wave, lane);
+            sync(p, S, hg + 1, lds_addr, wave);
             if (t < tl) {
                 const int key0 = t * BN;
                 // scalar: only tiles crossing the diagonal or the block end mask
@@ -381,7 +406,7 @@ struct Kernel {
                 softmax_phase(p, S, key0, mask, wrow0, lane);
             }
         }
-        if (grp == 0) sync(p, S, 2 * ntiles + 1, lds_addr, kbase, vbase, kstride, wave, lane);
+        if (grp == 0) sync(p, S, 2 * ntiles + 1, lds_addr, wave);
         // copies issued past the end land in stages nobody reads; retire them
         // before the workgroup's LDS is handed to the next workgroup
         wait_vmcnt<0>();

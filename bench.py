@@ -7,6 +7,11 @@ measured rank (cpattn_step_fwd; at step i the rank reads the K/V block of
 rank (rank - i) mod cp) and the LSE merge (cpattn_merge).  W untimed
 warm-up steps, then K timed steps bracketed by synchronisation.
 
+The same share is also timed through the fused form (the split, then one
+cpattn_forward_fused launch that carries the online softmax across the cp
+key blocks, so there are no partials and no merge) and reported under
+"fused".
+
 value = causal-effective FLOPs of the rank's share (4*d per visible query/
 key pair) / the measured time of a step.  Per-kernel times come from HIP
 events recorded on the stream the kernels run on.
@@ -39,8 +44,9 @@ def parse():
     return ap.parse_args()
 
 
-def committed_traffic(workload):
-    """HBM bytes per attention launch from the committed counter summary.
+def committed_traffic(workload, key="attention_traffic_bytes_per_launch"):
+    """HBM bytes per launch of the attention kernel (key: the step kernel's
+    or the fused kernel's line) from the committed counter summary.
 
     The summary records the sha256 of the kernel source it was measured
     with; if the source has changed since, the figure no longer describes
@@ -58,7 +64,7 @@ def committed_traffic(workload):
         for line in f:
             if "kernel source sha256" in line:
                 recorded = line.rsplit(":", 1)[1].strip()
-            if line.startswith("attention_traffic_bytes_per_launch:"):
+            if line.startswith(key + ":"):
                 traffic = float(line.split(":", 1)[1])
     return traffic if recorded == digest else None
 
@@ -147,6 +153,29 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
+    # the fused form of the same share: split, then one launch
+    fused = None
+    if w.dtype == "bf16":
+        fout = P.alloc_out(rank, C.CPATTN_F32)
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                P.partition(stream)
+                P.forward_fused(fout, stream)
+            torch.cuda.synchronize()
+            f_total, f_attn = [], []
+            for _ in range(args.steps):
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record(stream)
+                P.partition(stream)
+                e1.record(stream)
+                P.forward_fused(fout, stream)
+                e2.record(stream)
+                f_total.append((e0, e2))
+                f_attn.append((e1, e2))
+            torch.cuda.synchronize()
+        fused = {"ms": float(np.mean([a.elapsed_time(b) for a, b in f_total])),
+                 "attn_ms": float(np.mean([a.elapsed_time(b) for a, b in f_attn]))}
+
     # per-kernel times (ms) from the events, averaged over the timed steps
     part_ms, merge_ms, step_ms, total_ms = [], [], [[] for _ in range(w.cp)], []
     for evs in all_evs:
@@ -206,6 +235,18 @@ def main():
         "rank_flops": flops,
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
     }
+    if fused is not None:
+        f_tf = flops / (fused["attn_ms"] * 1e-3) / 1e12
+        line["fused"] = {
+            "entry_point": "cpattn_forward_fused",
+            "ms_per_step": round(fused["ms"], 4),
+            "value": round(flops / (fused["ms"] * 1e-3) / 1e12, 2),
+            "kernel": "attn_fused_bf16",
+            "avg_launch_ms": round(fused["attn_ms"], 4),
+            "achieved": round(f_tf, 2),
+            "frac": round(f_tf / peak, 4),
+            "traffic": committed_traffic(w.name, "fused_traffic_bytes_per_launch"),
+        }
     if args.cpu_sample_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, rank, args.cpu_sample_seconds)
     else:

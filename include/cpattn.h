@@ -168,6 +168,23 @@ int cpattn_forward(const cpattn_dims *dims, int dtype, float scale, int rank,
                    size_t ws_bytes, int out_dtype, void *o_out, float *lse_out,
                    void *stream);
 
+/* One rank's whole forward share in one launch, device ("超大规模集群…":
+ * the rank's big and small attention run concurrently; "Megatron-LM 篇" 3.2
+ * step 2 and its per-step LSE correction).  Each query row's online softmax
+ * runs on through the key blocks of all cp steps of cpattn_step_mode
+ * (kv_first_half halves of ranks r-1..0, q_second_half blocks of ranks
+ * cp-1..r+1 for rows c..2c-1, the causal block of rank r), so the per-step
+ * correction happens in place: no partials, no merge, no workspace.  The
+ * result is the one cpattn_forward gives, up to rounding order.
+ * qz, kz, vz: partitioned [cp, b, 2c, h, d] bf16 (CPATTN_BF16 only,
+ * EDTYPE otherwise; d = 128, ESHAPE otherwise).  o_out [b, 2c, hq, d] in
+ * out_dtype (CPATTN_F32, or CPATTN_BF16 rounded to nearest even); lse_out
+ * [b, hq, 2c] fp32 natural log, or NULL.  Pointers 16-byte aligned (lse_out
+ * 4-byte), EALIGN otherwise.  Asynchronous on 'stream'. */
+int cpattn_forward_fused(const cpattn_dims *dims, int dtype, float scale, int rank,
+                         const void *qz, const void *kz, const void *vz, int out_dtype,
+                         void *o_out, float *lse_out, void *stream);
+
 /* Static name of a status code. */
 const char *cpattn_status_str(int status);
 

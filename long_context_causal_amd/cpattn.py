@@ -70,10 +70,12 @@ def lib():
         L.cpattn_forward_workspace.restype = ctypes.c_size_t
         L.cpattn_forward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, ctypes.c_size_t,
                                      I, P, P, P]
+        L.cpattn_forward_fused.argtypes = [D, I, ctypes.c_float, I, P, P, P, I, P, P, P]
         L.cpattn_status_str.argtypes = [I]
         L.cpattn_status_str.restype = ctypes.c_char_p
         for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
-                     "cpattn_step_fwd", "cpattn_merge", "cpattn_forward"):
+                     "cpattn_step_fwd", "cpattn_merge", "cpattn_forward",
+                     "cpattn_forward_fused"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -157,3 +159,11 @@ def cpattn_forward(dims, dtype, scale, rank, qz, kz, vz, ws, ws_bytes, out_dtype
                                 _ptr(kz), _ptr(vz), _ptr(ws), int(ws_bytes), out_dtype,
                                 _ptr(o_out), _ptr(lse_out), _stream(stream)),
            "cpattn_forward")
+
+
+def cpattn_forward_fused(dims, dtype, scale, rank, qz, kz, vz, out_dtype, o_out, lse_out=None,
+                         stream=None):
+    _check(lib().cpattn_forward_fused(ctypes.byref(dims), dtype, float(scale), rank, _ptr(qz),
+                                      _ptr(kz), _ptr(vz), out_dtype, _ptr(o_out), _ptr(lse_out),
+                                      _stream(stream)),
+           "cpattn_forward_fused")

@@ -235,4 +235,32 @@ int cpattn_forward(const cpattn_dims *dims, int dtype, float scale, int rank, co
     return cpattn_merge(dims, dims->cp, parts, out_dtype, o_out, lse_out, stream);
 }
 
+int cpattn_forward_fused(const cpattn_dims *dims, int dtype, float scale, int rank,
+                         const void *qz, const void *kz, const void *vz, int out_dtype,
+                         void *o_out, float *lse_out, void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (rank < 0 || rank >= dims->cp) return CPATTN_EINVAL;
+    if (!qz || !kz || !vz || !o_out) return CPATTN_EINVAL;
+    if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if (out_dtype != CPATTN_F32 && out_dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if (dims->d != 128) return CPATTN_ESHAPE;
+    if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz) || !aligned16(o_out) ||
+        (lse_out && ((uintptr_t)lse_out & 3u)))
+        return CPATTN_EALIGN;
+    const StepGeom g = cpattn::step_geom(*dims, CPATTN_CAUSAL, scale);
+    cpattn::FusedGeom f;
+    f.b = dims->b;
+    f.two_c = g.two_c;
+    f.hq = dims->hq;
+    f.hkv = dims->hkv;
+    f.rank = rank;
+    f.cp = dims->cp;
+    f.scale_log2 = g.scale_log2;
+    const hipError_t e = cpattn::launch_fused_bf16(f, qz, kz, vz, o_out,
+                                                   out_dtype == CPATTN_BF16, lse_out,
+                                                   (hipStream_t)stream);
+    return e == hipSuccess ? CPATTN_OK : CPATTN_EHIP;
+}
+
 }  // extern "C"

@@ -1,11 +1,22 @@
-// Blockwise attention of one CP step, bf16 inputs, fp32 accumulation, on
-// gfx950 matrix cores.
+// Blockwise attention of one CP step, and of a rank's whole share in one
+// launch, bf16 inputs, fp32 accumulation, on gfx950 matrix cores.
 //
 // What it computes ("Megatron-LM 篇", Context Parallel 3.2 step 2 and 3.4):
 // for each query row i of the step and head h, softmax attention over the
 // visible keys of the source rank's block, returning the normalised O_i and
 // the natural-log LSE L_i.  The mode decides the rows and keys (see
 // internal.h: q_row0, nq, nk, causal).
+//
+// The fused form ("超大规模集群…", the big and small attention of one rank
+// run concurrently; "Megatron-LM 篇" 3.2 step 2, the per-step LSE
+// correction): one workgroup streams, for its query rows, the key blocks of
+// all cp steps of the rank one after another -- the first halves of the
+// blocks of ranks r-1 .. 0, then (rows of the second chunk only) the whole
+// blocks of ranks cp-1 .. r+1, then the rank's own block under the causal
+// mask -- and keeps one running max, sum and accumulator across them.
+// Carrying the online softmax from one block to the next is the per-step
+// L/O correction done in place, so the result is the merged O and L with
+// no per-step partials.
 //
 // Work decomposition
 //   workgroup = 8 waves = 256 query rows of one (batch, head); each wave
@@ -82,10 +93,101 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units a stale max may lag
 
 struct Params {
     const uint16_t *q, *k, *v;
-    float *o, *lse;
+    void *o;                 // fp32, or bf16 for the fused form's bf16 output
+    float *lse;
     int64_t two_c, q_row0;
     int nq, nk, hq, hkv, group, num_qtiles;
     float scale_log2;
+    // fused form: the rank, the ring size and the element stride between
+    // the partitioned blocks of consecutive ranks
+    int rank, cp;
+    int64_t block_elems;
+};
+
+// One tile of the key sequence a workgroup streams: the block it comes from
+// (K and V bases of the workgroup's batch and KV head), its first key in the
+// block, the keys of the block visible in this segment, whether the causal
+// mask applies, and the first query row that sees the segment at all.
+struct TileRef {
+    const uint16_t *kb, *vb;
+    int key0, nk;
+    bool causal;
+    int min_row;
+};
+
+// One CP step: the source rank's block, the mode's keys.
+template <bool CAUSAL>
+struct StepPlan {
+    static constexpr bool kLongestFirst = CAUSAL;   // later causal tiles see more keys
+    const uint16_t *kb, *vb;
+    int nk, ntiles;
+    __device__ __forceinline__ void init(const Params &p, int qtile, int n, int g) {
+        kb = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
+        vb = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
+        nk = p.nk;
+        const int kend = CAUSAL ? min(p.nk, qtile * BM + BM) : p.nk;
+        ntiles = (kend + BN - 1) / BN;
+    }
+    // tiles past the last (copied ahead, never computed) repeat the last
+    __device__ __forceinline__ TileRef tile(int u) const {
+        return TileRef{kb, vb, min(u, ntiles - 1) * BN, nk, CAUSAL, 0};
+    }
+    // whether the wave whose rows start at wrow0 computes tile t: causal
+    // waves stop after their diagonal
+    __device__ __forceinline__ bool comp(int t, int wrow0) const {
+        if (t < 0) return false;
+        return CAUSAL ? t < min(ntiles, (wrow0 + 31) / BN + 1) : t < ntiles;
+    }
+};
+
+// A rank's whole share.  Segments in streaming order: ranks r-1 .. 0, keys
+// [0, c) (steps 1 .. r, kv_first_half); ranks cp-1 .. r+1, keys [0, 2c)
+// (steps r+1 .. cp-1, q_second_half: only rows c .. 2c-1 see them, and the
+// segments are streamed only when some row of the workgroup is one of
+// those); rank r, keys [0, min(2c, q0 + BM)) causal (step 0).  A segment
+// whose length is not a multiple of BN ends in a masked tile.
+struct FusedPlan {
+    static constexpr bool kLongestFirst = true;     // later tiles: second chunk, causal
+    const uint16_t *k0, *v0;      // rank 0's block, this batch and KV head
+    int64_t block;                // elements between consecutive ranks' blocks
+    int r, cp, c, cA, nAB, cB, ta, tb, kend, ntiles, q0;
+    __device__ __forceinline__ void init(const Params &p, int qtile, int n, int g) {
+        k0 = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
+        v0 = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
+        block = p.block_elems;
+        r = p.rank;
+        cp = p.cp;
+        c = (int)(p.two_c >> 1);
+        q0 = qtile * BM;
+        cA = (c + BN - 1) / BN;
+        cB = (2 * c + BN - 1) / BN;
+        nAB = (q0 + BM > c) ? cp - 1 - r : 0;
+        ta = r * cA;
+        tb = ta + nAB * cB;
+        kend = min(2 * c, q0 + BM);
+        ntiles = tb + (kend + BN - 1) / BN;
+    }
+    __device__ __forceinline__ TileRef tile(int u) const {
+        u = min(u, ntiles - 1);
+        if (u < ta) {
+            const int seg = u / cA;
+            const int64_t off = (int64_t)(r - 1 - seg) * block;
+            return TileRef{k0 + off, v0 + off, (u - seg * cA) * BN, c, false, 0};
+        }
+        if (u < tb) {
+            const int seg = (u - ta) / cB;
+            const int64_t off = (int64_t)(cp - 1 - seg) * block;
+            return TileRef{k0 + off, v0 + off, (u - ta - seg * cB) * BN, 2 * c, false, c};
+        }
+        const int64_t off = (int64_t)r * block;
+        return TileRef{k0 + off, v0 + off, (u - tb) * BN, kend, true, 0};
+    }
+    __device__ __forceinline__ bool comp(int t, int wrow0) const {
+        if (t < 0) return false;
+        if (t < ta) return true;
+        if (t < tb) return wrow0 + 31 >= c;
+        return t - tb < min(ntiles - tb, (wrow0 + 31) / BN + 1);
+    }
 };
 
 __device__ __forceinline__ int swap_bits23(int m) {
@@ -131,7 +233,7 @@ __device__ __forceinline__ void dma16(const void *base, unsigned off, unsigned l
                  : "memory");
 }
 
-template <bool CAUSAL>
+template <class Plan, bool OUT_BF16>
 struct Kernel {
     // Per-wave state.
     struct State {
@@ -144,18 +246,17 @@ struct Kernel {
         unsigned voff[D / 32];   // lane's byte offset of each V^T read in a stage
         unsigned gk[KI], gv[KI]; // lane's byte offsets of its K and V copies in a tile
         int krow[KI];            // tile row of each of the lane's copies
-        const uint16_t *kbase, *vbase;
         int64_t kstride;         // elements between consecutive keys
     };
 
-    // Issue this wave's share of the direct copies of tile `key0` into one
-    // LDS stage (K at sK, V at sK + TILEB): a scalar tile base plus the
-    // lane's fixed offsets.  A tile crossing the block end repeats row nk-1.
-    __device__ __forceinline__ static void issue(const Params &p, const State &S, unsigned sK,
-                                                 int key0, int wave) {
-        if (key0 + BN <= p.nk) {
-            const uint16_t *kb = S.kbase + (int64_t)key0 * S.kstride;
-            const uint16_t *vb = S.vbase + (int64_t)key0 * S.kstride;
+    // Issue this wave's share of the direct copies of one tile into an LDS
+    // stage (K at sK, V at sK + TILEB): a scalar tile base plus the lane's
+    // fixed offsets.  A tile crossing its segment end repeats row nk-1.
+    __device__ __forceinline__ static void issue(const State &S, unsigned sK, const TileRef &tr,
+                                                 int wave) {
+        if (tr.key0 + BN <= tr.nk) {
+            const uint16_t *kb = tr.kb + (int64_t)tr.key0 * S.kstride;
+            const uint16_t *vb = tr.vb + (int64_t)tr.key0 * S.kstride;
 #pragma unroll
             for (int i = 0; i < KI; ++i) {
                 const unsigned dst = sK + (wave * KI + i) * 4 * ROWB;
@@ -164,12 +265,12 @@ struct Kernel {
             }
         } else {
             // base row b0 <= every row copied, so lane offsets stay >= 0
-            const int b0 = max(min(key0, p.nk - BN), 0);
-            const uint16_t *kb = S.kbase + (int64_t)b0 * S.kstride;
-            const uint16_t *vb = S.vbase + (int64_t)b0 * S.kstride;
+            const int b0 = max(min(tr.key0, tr.nk - BN), 0);
+            const uint16_t *kb = tr.kb + (int64_t)b0 * S.kstride;
+            const uint16_t *vb = tr.vb + (int64_t)b0 * S.kstride;
 #pragma unroll
             for (int i = 0; i < KI; ++i) {
-                const int key = min(key0 + S.krow[i], p.nk - 1);
+                const int key = min(tr.key0 + S.krow[i], tr.nk - 1);
                 // gk holds krow rows; move the lane to row key - b0
                 const unsigned adj = (unsigned)((key - b0 - S.krow[i]) * (int)S.kstride * 2);
                 const unsigned dst = sK + (wave * KI + i) * 4 * ROWB;
@@ -222,8 +323,9 @@ struct Kernel {
     // Row max of the tile's raw scores; the masked variant first sets the
     // invisible scores to -inf (keys past the block, or after the row).
     template <bool MASK>
-    __device__ __forceinline__ static float tile_max(const Params &p, State &S, int key0,
-                                                     int qrow, int hi) {
+    __device__ __forceinline__ static float tile_max(const TileRef &tr, State &S, int qrow,
+                                                     int hi) {
+        const int key0 = tr.key0;
         float tmax = -INFINITY;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
@@ -232,7 +334,8 @@ struct Kernel {
                 float x = S.s[h2][e];
                 if constexpr (MASK) {
                     const int key = key0 + h2 * 32 + 16 * (e >> 3) + 8 * hi + (e & 7);
-                    const bool vis = key < p.nk && (!CAUSAL || key <= qrow);
+                    const bool vis =
+                        key < tr.nk && (!tr.causal || key <= qrow) && qrow >= tr.min_row;
                     x = vis ? x : -INFINITY;
                     S.s[h2][e] = x;
                 }
@@ -243,16 +346,22 @@ struct Kernel {
 
     // Vector phase: online softmax of S(t) into P(t), rescaling O and l
     // first when the running max moves by more than the slack.
-    __device__ __forceinline__ static void softmax_phase(const Params &p, State &S, int key0,
-                                                         bool mask, int wrow0, int lane) {
+    __device__ __forceinline__ static void softmax_phase(const Params &p, State &S,
+                                                         const TileRef &tr, int wrow0,
+                                                         int lane) {
         const int hi = lane >> 5;
         const int qrow = wrow0 + (lane & 31);
-        float tmax = mask ? tile_max<true>(p, S, key0, qrow, hi)
-                          : tile_max<false>(p, S, key0, qrow, hi);
+        // scalar: only tiles crossing the diagonal or the segment end, and
+        // waves that straddle a segment's first row, mask
+        const bool mask = (tr.key0 + BN > tr.nk) || (tr.causal && tr.key0 + BN - 1 > wrow0) ||
+                          wrow0 < tr.min_row;
+        float tmax = mask ? tile_max<true>(tr, S, qrow, hi) : tile_max<false>(tr, S, qrow, hi);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
         const float m_new = fmaxf(S.m_run, tmax);
         if (__builtin_amdgcn_ballot_w64(m_new > S.m_run + RESCALE_SLACK)) {
-            const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_new);
+            // a row that has seen no visible key yet (m = -inf) keeps alpha 1
+            const float alpha =
+                m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(S.m_run - m_new);
             S.l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) S.acc[dt] *= alpha;
@@ -282,14 +391,14 @@ struct Kernel {
     // The barrier opening half-iteration h.  At even h = 2u: this wave's
     // copies of tile u are complete before it (the copies of tile u+1 may
     // still fly), and the copies of tile u+2 are issued after it.
-    __device__ __forceinline__ static void sync(const Params &p, State &S, int h,
+    __device__ __forceinline__ static void sync(const Plan &P, State &S, int h,
                                                 unsigned lds_addr, int wave) {
         const bool even = (h & 1) == 0;
         if (even) wait_vmcnt<LPT>();
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (even) {
             const int u = (h >> 1) + 2;
-            issue(p, S, lds_addr + (u % NS) * 2 * TILEB, u * BN, wave);
+            issue(S, lds_addr + (u % NS) * 2 * TILEB, P.tile(u), wave);
         }
     }
 
@@ -317,16 +426,13 @@ struct Kernel {
         const int g = item % p.hkv;
         const int n = item / p.hkv;
         const int head = g * p.group + hh;
-        const int qtile = CAUSAL ? p.num_qtiles - 1 - qt_rank : qt_rank;
+        const int qtile = Plan::kLongestFirst ? p.num_qtiles - 1 - qt_rank : qt_rank;
         const int wrow0 = qtile * BM + wave * 32;   // first step row of this wave
 
-        const int kend = CAUSAL ? min(p.nk, qtile * BM + BM) : p.nk;
-        const int ntiles = (kend + BN - 1) / BN;
-        // tiles this wave computes: causal waves stop at their diagonal
-        const int tl = CAUSAL ? min(ntiles, (wrow0 + 31) / BN + 1) : ntiles;
+        Plan P;
+        P.init(p, qtile, n, g);
+        const int ntiles = P.ntiles;
         State S;
-        S.kbase = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
-        S.vbase = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
         S.kstride = (int64_t)p.hkv * D;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
@@ -371,8 +477,8 @@ struct Kernel {
         // prologue: tiles 0 and 1 in flight, then Q; one full wait before the
         // loop (tile 0 has to land first anyway) also tells the compiler that
         // Q is resident, so it puts no memory wait inside the loop
-        issue(p, S, lds_addr, 0, wave);
-        issue(p, S, lds_addr + 2 * TILEB, BN, wave);
+        issue(S, lds_addr, P.tile(0), wave);
+        issue(S, lds_addr + 2 * TILEB, P.tile(1), wave);
         {
             const int row = min(wrow0 + l32, p.nq - 1);
             const uint16_t *src =
@@ -390,33 +496,39 @@ struct Kernel {
         // tile u+2 is copied into the stage tile u-2 left (its last reader ran
         // at h-1).  The trailing group's first and the leading group's last
         // half-iteration are idle.
-        if (grp == 1) sync(p, S, 0, lds_addr, wave);
+        // A wave computes tile t when P.comp(t): the matrix phase G(t) runs
+        // when it needs S(t) or adds P(t-1); after a tile the wave skips, P is
+        // zero, so a following G adds nothing for it.
+        if (grp == 1) sync(P, S, 0, lds_addr, wave);
         for (int t = 0; t <= ntiles; ++t) {
             const int hg = 2 * t + grp;
-            sync(p, S, hg, lds_addr, wave);
-            if (t <= tl)
+            sync(P, S, hg, lds_addr, wave);
+            if (P.comp(t, wrow0) || P.comp(t - 1, wrow0))
                 matrix_phase(S, lds_addr + (t % NS) * 2 * TILEB,
                              lds_addr + ((t + NS - 1) % NS) * 2 * TILEB + TILEB);
             if (t == ntiles) break;
-            sync(p, S, hg + 1, lds_addr, wave);
-            if (t < tl) {
-                const int key0 = t * BN;
-                // scalar: only tiles crossing the diagonal or the block end mask
-                const bool mask = (key0 + BN > p.nk) || (CAUSAL && key0 + BN - 1 > wrow0);
-                softmax_phase(p, S, key0, mask, wrow0, lane);
+            sync(P, S, hg + 1, lds_addr, wave);
+            if (P.comp(t, wrow0)) {
+                softmax_phase(p, S, P.tile(t), wrow0, lane);
+            } else {
+#pragma unroll
+                for (int kc = 0; kc < BN / 16; ++kc)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) S.pf[kc][e] = (__bf16)0.0f;
             }
         }
-        if (grp == 0) sync(p, S, 2 * ntiles + 1, lds_addr, wave);
+        if (grp == 0) sync(P, S, 2 * ntiles + 1, lds_addr, wave);
         // copies issued past the end land in stages nobody reads; retire them
         // before the workgroup's LDS is handed to the next workgroup
         wait_vmcnt<0>();
 
-        // Normalise and store O_i (fp32) and L_i (natural log).
+        // Normalise and store O (fp32, or bf16 rounded to nearest even) and
+        // L (natural log).
         const float lt = S.l_run + __shfl_xor(S.l_run, 32);
         const int row = wrow0 + l32;
         if (row < p.nq) {
             const float inv = 1.0f / lt;
-            float *dst = p.o + ((n * (int64_t)p.nq + row) * p.hq + head) * D + 4 * hi;
+            const int64_t base = ((n * (int64_t)p.nq + row) * p.hq + head) * D + 4 * hi;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -424,26 +536,49 @@ struct Kernel {
                     f32x4 w;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) w[j] = S.acc[dt][i * 4 + j] * inv;
-                    *(f32x4 *)(dst + dt * 32 + i * 8) = w;
+                    if constexpr (OUT_BF16) {
+                        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                        *(bf16x4 *)((__bf16 *)p.o + base + dt * 32 + i * 8) =
+                            __builtin_convertvector(w, bf16x4);
+                    } else {
+                        *(f32x4 *)((float *)p.o + base + dt * 32 + i * 8) = w;
+                    }
                 }
-            if (hi == 0)
+            if (hi == 0 && p.lse != nullptr)
                 p.lse[((int64_t)n * p.hq + head) * p.nq + row] =
                     (S.m_run + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
         }
     }
 };
 
+// One CP step (fp32 partial output).
 template <bool CAUSAL>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_step_bf16(Params p) {
     __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
-    Kernel<CAUSAL>::run(p, lds);
+    Kernel<StepPlan<CAUSAL>, false>::run(p, lds);
 }
 
-template <bool CAUSAL>
-hipError_t launch(const StepGeom &g, const void *q, const void *k, const void *v, float *o,
-                  float *lse, hipStream_t stream) {
-    Params p;
+// A rank's whole share (merged output, fp32 or bf16).
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fused_bf16(Params p) {
+    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
+    Kernel<FusedPlan, OUT_BF16>::run(p, lds);
+}
+
+template <class KernelFn>
+hipError_t launch_kernel(KernelFn fn, const Params &p, int64_t b, int hq, hipStream_t stream) {
+    const int64_t blocks = (int64_t)p.num_qtiles * hq * b;
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, const void *v,
+                            float *o, float *lse, hipStream_t stream) {
+    Params p = {};
     p.q = (const uint16_t *)q;
     p.k = (const uint16_t *)k;
     p.v = (const uint16_t *)v;
@@ -458,18 +593,33 @@ hipError_t launch(const StepGeom &g, const void *q, const void *k, const void *v
     p.group = g.hq / g.hkv;
     p.num_qtiles = (int)((g.nq + BM - 1) / BM);
     p.scale_log2 = g.scale_log2;
-    const int64_t blocks = (int64_t)p.num_qtiles * g.hq * g.b;
-    hipLaunchKernelGGL((attn_step_bf16<CAUSAL>), dim3((unsigned)blocks), dim3(64 * NW), 0,
-                       stream, p);
-    return hipGetLastError();
+    if (g.causal) return launch_kernel(attn_step_bf16<true>, p, g.b, g.hq, stream);
+    return launch_kernel(attn_step_bf16<false>, p, g.b, g.hq, stream);
 }
 
-}  // namespace
-
-hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, const void *v,
-                            float *o, float *lse, hipStream_t stream) {
-    if (g.causal) return launch<true>(g, q, k, v, o, lse, stream);
-    return launch<false>(g, q, k, v, o, lse, stream);
+hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz, const void *vz,
+                             void *o, bool out_bf16, float *lse, hipStream_t stream) {
+    Params p = {};
+    const int64_t block_q = f.b * f.two_c * f.hq * D;     // one rank's Q block, elements
+    p.q = (const uint16_t *)qz + f.rank * block_q;
+    p.k = (const uint16_t *)kz;
+    p.v = (const uint16_t *)vz;
+    p.o = o;
+    p.lse = lse;
+    p.two_c = f.two_c;
+    p.q_row0 = 0;
+    p.nq = (int)f.two_c;
+    p.nk = (int)f.two_c;
+    p.hq = f.hq;
+    p.hkv = f.hkv;
+    p.group = f.hq / f.hkv;
+    p.num_qtiles = (int)((f.two_c + BM - 1) / BM);
+    p.scale_log2 = f.scale_log2;
+    p.rank = f.rank;
+    p.cp = f.cp;
+    p.block_elems = f.b * f.two_c * f.hkv * D;
+    if (out_bf16) return launch_kernel(attn_fused_bf16<true>, p, f.b, f.hq, stream);
+    return launch_kernel(attn_fused_bf16<false>, p, f.b, f.hq, stream);
 }
 
 }  // namespace cpattn

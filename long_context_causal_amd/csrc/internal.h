@@ -33,6 +33,20 @@ hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k,
                             const void *v, float *o, float *lse,
                             hipStream_t stream);
 
+// Geometry of one rank's fused share (cpattn_forward_fused).
+struct FusedGeom {
+    int64_t b;
+    int64_t two_c;
+    int32_t hq, hkv, rank, cp;
+    float scale_log2;
+};
+
+// qz, kz, vz: the partitioned tensors of all ranks [cp, b, 2c, h, 128] bf16.
+// o: [b, 2c, hq, 128] fp32, or bf16 when out_bf16; lse: [b, hq, 2c] or null.
+hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
+                             const void *vz, void *o, bool out_bf16, float *lse,
+                             hipStream_t stream);
+
 hipError_t launch_step_f32(const StepGeom &g, const void *q, const void *k,
                            const void *v, float *o, float *lse,
                            hipStream_t stream);

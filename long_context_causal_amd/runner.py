@@ -103,6 +103,23 @@ class CPProblem:
                          buf["ws"], buf["ws_bytes"], buf["out_dtype"], buf["o"], buf["lse"],
                          stream)
 
+    # --- the same share in one launch ----------------------------------------
+    def alloc_out(self, rank, out_dtype=None):
+        """Output buffers of ``rank``'s share (the fused form needs no workspace)."""
+        out_dtype = self.dtype if out_dtype is None else out_dtype
+        two_c = 2 * self.c
+        o = torch.empty((self.b, two_c, self.w.hq, self.w.d),
+                        dtype=torch.bfloat16 if out_dtype == C.CPATTN_BF16 else torch.float32,
+                        device=self.device)
+        lse = torch.empty((self.b, self.w.hq, two_c), dtype=torch.float32, device=self.device)
+        return dict(o=o, lse=lse, out_dtype=out_dtype, rank=rank)
+
+    def forward_fused(self, out, stream=None, scale=0.0, with_lse=True):
+        """The whole share through cpattn_forward_fused (one launch)."""
+        C.cpattn_forward_fused(self.dims, self.dtype, scale, out["rank"], self.qz, self.kz,
+                               self.vz, out["out_dtype"], out["o"],
+                               out["lse"] if with_lse else None, stream)
+
 
 def _round256(x):
     return (x + 255) // 256 * 256

@@ -160,3 +160,33 @@ def test_forward_workspace_and_validation():
 def test_binding_names_match_header():
     for name in _declared_functions():
         assert hasattr(C, name), name
+
+
+def test_forward_fused_validation_before_launch():
+    L = C.lib()
+    d = _dims(b=1, s=32768, hq=64, hkv=8, d=128, cp=8)
+    args = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), 3, ALIGNED, ALIGNED, ALIGNED,
+            C.CPATTN_F32, ALIGNED, None, 0]
+    bad_dtype = list(args)
+    bad_dtype[1] = C.CPATTN_F32                    # the fused form is bf16 only
+    assert L.cpattn_forward_fused(*bad_dtype) == C.CPATTN_EDTYPE
+    bad_out = list(args)
+    bad_out[7] = 9
+    assert L.cpattn_forward_fused(*bad_out) == C.CPATTN_EDTYPE
+    bad_rank = list(args)
+    bad_rank[3] = 8
+    assert L.cpattn_forward_fused(*bad_rank) == C.CPATTN_EINVAL
+    bad_align = list(args)
+    bad_align[8] = ALIGNED + 8
+    assert L.cpattn_forward_fused(*bad_align) == C.CPATTN_EALIGN
+    null_q = list(args)
+    null_q[4] = None
+    assert L.cpattn_forward_fused(*null_q) == C.CPATTN_EINVAL
+    d64 = _dims(b=1, s=32768, hq=64, hkv=8, d=64, cp=8)
+    bad_d = list(args)
+    bad_d[0] = ctypes.byref(d64)
+    assert L.cpattn_forward_fused(*bad_d) == C.CPATTN_ESHAPE
+    bad_s = _dims(b=1, s=1000, hq=64, hkv=8, d=128, cp=8)   # s % 2cp != 0
+    bad_shape = list(args)
+    bad_shape[0] = ctypes.byref(bad_s)
+    assert L.cpattn_forward_fused(*bad_shape) == C.CPATTN_ESHAPE

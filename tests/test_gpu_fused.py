@@ -1,0 +1,107 @@
+"""GPU fused per-rank forward (cpattn_forward_fused: all cp steps of a rank
+in one launch, the per-step LSE correction carried in the online softmax)
+vs the non-CP oracle and vs the step-wise entry point.
+
+* every bf16 workload at a reduced length (ragged chunks and tiles, GQA,
+  MHA, RoPE, b = 2): every rank, every row, every head vs the oracle;
+* every bf16 workload at its full size: sampled rows (chunk edges plus
+  random rows) of every rank (the RoPE workload: its measured rank);
+* the fused and the step-wise results agree within the bf16 bound on the
+  whole share; the bf16 output is the fp32 output within one rounding;
+  lse_out = NULL leaves O unchanged; cp = 1 is plain causal attention.
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import (BF16_MAX_ABS, BF16_MEAN_ABS, C, CPProblem, assert_close, host_f32,
+                         make_inputs, ocp, oracle_full, oracle_sampled_rows, run_rank,
+                         sample_local_rows, say, small, torch)
+from long_context_causal_amd.inputs import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fused(P, rank, out_dtype=C.CPATTN_F32, with_lse=True):
+    out = P.alloc_out(rank, out_dtype)
+    P.forward_fused(out, with_lse=with_lse)
+    torch.cuda.synchronize()
+    return host_f32(out["o"]), out["lse"].cpu().numpy()
+
+
+REDUCED = [("bf16_gqa_s8k_cp4", 2 * 4 * 100, None),            # c = 100: ragged tiles
+           ("bf16_gqa_s32k_cp8", 2 * 8 * 40, None),             # c = 40 < one tile
+           ("bf16_mha_s16k_cp4_widelogits", 2 * 4 * 96, None),
+           ("bf16_gqa_s128k_cp16_rope", 2 * 16 * 24, None),
+           ("bf16_gqa_s8k_cp4", 2 * 4 * 256, 3),                # whole tiles, b = 3
+           ("bf16_gqa_s32k_cp8", 2 * 8 * 320, None)]            # straddling query tiles
+
+
+@pytest.mark.parametrize("name,s,b", REDUCED)
+def test_fused_reduced_all_ranks(name, s, b):
+    w = small(WORKLOADS[name], s, b)
+    say(f"fused reduced {name} s={s} b={w.b}")
+    q, k, v = make_inputs(w)
+    o_full, l_full = oracle_full(w, q, k, v)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    for r in range(w.cp):
+        o, l = run_fused(P, r)
+        pos = ocp.zigzag_positions(w.s, w.cp, r)
+        assert_close(f"rank {r} O", o, o_full[:, pos], BF16_MAX_ABS, BF16_MEAN_ABS)
+        assert_close(f"rank {r} L", l, l_full[:, :, pos], 1e-3)
+
+
+def test_fused_cp1_is_plain_causal():
+    w = small(WORKLOADS["bf16_gqa_s8k_cp4"], 704)
+    import dataclasses
+    w = dataclasses.replace(w, cp=1)
+    say("fused cp=1")
+    q, k, v = make_inputs(w)
+    o_full, l_full = oracle_full(w, q, k, v)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    o, l = run_fused(P, 0)
+    assert_close("O", o, o_full, BF16_MAX_ABS, BF16_MEAN_ABS)
+    assert_close("L", l, l_full, 1e-3)
+
+
+def test_fused_matches_stepwise_and_options():
+    w = small(WORKLOADS["bf16_gqa_s32k_cp8"], 2 * 8 * 192)
+    say("fused vs step-wise, options")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    for r in range(w.cp):
+        o_s, l_s = run_rank(P, r, C.CPATTN_F32)
+        o_f, l_f = run_fused(P, r)
+        assert_close(f"rank {r} O fused vs steps", o_f, o_s, BF16_MAX_ABS, BF16_MEAN_ABS)
+        assert_close(f"rank {r} L fused vs steps", l_f, l_s, 1e-3)
+    r = w.rank
+    o32, l32 = run_fused(P, r)
+    ob, _ = run_fused(P, r, C.CPATTN_BF16)
+    assert np.all(np.abs(ob - o32) <= np.abs(o32) * 2.0 ** -8 + 1e-30), "bf16 output rounding"
+    on, _ = run_fused(P, r, with_lse=False)
+    assert np.array_equal(on, o32), "lse_out = NULL changed O"
+
+
+FULL = [("bf16_gqa_s8k_cp4", 12), ("bf16_mha_s16k_cp4_widelogits", 8),
+        ("bf16_gqa_s32k_cp8", 6), ("bf16_gqa_s128k_cp16_rope", 24)]
+
+
+@pytest.mark.parametrize("name,n_mid", FULL)
+def test_fused_full_size_sampled_rows(name, n_mid):
+    w = WORKLOADS[name]
+    say(f"fused full {name}: inputs")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    ranks = [w.rank] if w.rope_theta is not None else list(range(w.cp))
+    for r in ranks:
+        say(f"  rank {r}: gpu")
+        o, l = run_fused(P, r)
+        rows = sample_local_rows(w.c, n_mid, seed=200 + r)
+        pos = ocp.zigzag_positions(w.s, w.cp, r)[rows]
+        say(f"  rank {r}: oracle on {len(rows)} rows")
+        o_ref, l_ref = oracle_sampled_rows(w, q, k, v, pos)
+        assert_close(f"rank {r} O", o[:, rows], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+        assert_close(f"rank {r} L", l[:, :, rows], l_ref, 1e-3)

@@ -115,3 +115,113 @@ int oracle_attention(const double *q, const double *k, const double *v,
     }
     return failed ? -1 : 0;
 }
+
+/*
+ * Backward of the same attention, in fp64: the gradients of a scalar loss
+ * whose gradient with respect to O is dO.  The pages name the backward only
+ * through the communication it adds under context parallelism ("超大规模集群…",
+ * "CP 与其他技术结合": an all-gather of K/V and a reduce-scatter of their
+ * gradients); the arithmetic is the derivative of the definition above,
+ * written out.  For every batch n, query head h and query row i:
+ *
+ *     P_j   = exp(z_j - L)                         (the softmax weights)
+ *     O[t]  = sum_j P_j v_j[t]                     (recomputed, as above)
+ *     D     = sum_t dO[t] O[t]
+ *     dP_j  = sum_t dO[t] v_j[t]
+ *     dS_j  = P_j (dP_j - D)                       (softmax derivative)
+ *     dq[t] = scale * sum_j dS_j k_j[t]
+ *     dk_j[t] += scale * dS_j q[t]                 (summed over every row i
+ *     dv_j[t] += P_j dO[t]                          and every head h of the
+ *                                                   group g of head h)
+ *
+ * Work is split over (batch, KV head) so every dk/dv row has one writer;
+ * inside a group, heads ascend, then rows, then keys.
+ *
+ * Layouts: q, dq, dout [b, nq, hq, d]; k, v, dk, dv [b, nk, hkv, d];
+ * kend [nq].  dq, dk and dv are overwritten.
+ */
+int oracle_attention_bwd(const double *q, const double *k, const double *v,
+                         const double *dout, int64_t b, int64_t nq, int64_t nk,
+                         int64_t hq, int64_t hkv, int64_t d, double scale,
+                         const int64_t *kend, double *dq, double *dk, double *dv,
+                         int nthreads) {
+    if (!q || !k || !v || !dout || !kend || !dq || !dk || !dv) return -1;
+    if (b < 0 || nq < 0 || nk < 0 || hq <= 0 || hkv <= 0 || d <= 0) return -1;
+    if (hq % hkv != 0) return -1;
+    for (int64_t i = 0; i < nq; ++i)
+        if (kend[i] < 0 || kend[i] > nk) return -1;
+    const int64_t group = hq / hkv;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel
+    {
+        const size_t nkz = (size_t)(nk > 0 ? nk : 1);
+        double *z = (double *)malloc(sizeof(double) * nkz);
+        double *o = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!z || !o) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t item = 0; item < b * hkv; ++item) {
+            if (!z || !o) continue;
+            const int64_t n = item / hkv, g = item % hkv;
+            for (int64_t j = 0; j < nk; ++j)
+                for (int64_t t = 0; t < d; ++t) {
+                    dk[((n * nk + j) * hkv + g) * d + t] = 0.0;
+                    dv[((n * nk + j) * hkv + g) * d + t] = 0.0;
+                }
+            for (int64_t h = g * group; h < (g + 1) * group; ++h)
+                for (int64_t i = 0; i < nq; ++i) {
+                    const int64_t kn = kend[i];
+                    const double *qi = q + ((n * nq + i) * hq + h) * d;
+                    const double *doi = dout + ((n * nq + i) * hq + h) * d;
+                    double *dqi = dq + ((n * nq + i) * hq + h) * d;
+                    for (int64_t t = 0; t < d; ++t) dqi[t] = 0.0;
+                    if (kn == 0) continue;
+                    for (int64_t j = 0; j < kn; ++j) {
+                        const double *kj = k + ((n * nk + j) * hkv + g) * d;
+                        double dot = 0.0;
+                        for (int64_t t = 0; t < d; ++t) dot += qi[t] * kj[t];
+                        z[j] = scale * dot;
+                    }
+                    double m = z[0];
+                    for (int64_t j = 1; j < kn; ++j)
+                        if (z[j] > m) m = z[j];
+                    double s = 0.0;
+                    for (int64_t j = 0; j < kn; ++j) s += exp(z[j] - m);
+                    const double lse = m + log(s);
+                    for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
+                    for (int64_t j = 0; j < kn; ++j) {
+                        const double p = exp(z[j] - lse);
+                        const double *vj = v + ((n * nk + j) * hkv + g) * d;
+                        for (int64_t t = 0; t < d; ++t) o[t] += p * vj[t];
+                    }
+                    double dd = 0.0;
+                    for (int64_t t = 0; t < d; ++t) dd += doi[t] * o[t];
+                    for (int64_t j = 0; j < kn; ++j) {
+                        const double p = exp(z[j] - lse);
+                        const double *kj = k + ((n * nk + j) * hkv + g) * d;
+                        const double *vj = v + ((n * nk + j) * hkv + g) * d;
+                        double *dkj = dk + ((n * nk + j) * hkv + g) * d;
+                        double *dvj = dv + ((n * nk + j) * hkv + g) * d;
+                        double dp = 0.0;
+                        for (int64_t t = 0; t < d; ++t) dp += doi[t] * vj[t];
+                        const double ds = p * (dp - dd);
+                        for (int64_t t = 0; t < d; ++t) {
+                            dqi[t] += scale * ds * kj[t];
+                            dkj[t] += scale * ds * qi[t];
+                            dvj[t] += p * doi[t];
+                        }
+                    }
+                }
+        }
+        free(z);
+        free(o);
+    }
+    return failed ? -1 : 0;
+}

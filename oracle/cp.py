@@ -238,3 +238,87 @@ def causal_flops(b, s, hq, d, cp, rank=None):
 
 def default_scale(d):
     return 1.0 / math.sqrt(d)
+
+
+# --- backward ---------------------------------------------------------------
+# The pages treat the backward only through the communication context
+# parallelism adds to it ("超大规模集群…", "CP 与其他技术结合": an all-gather
+# of K/V and a reduce-scatter of the K/V gradients).  Each ring step of the
+# forward has a backward counterpart on the same blocks; it uses the rank's
+# final (merged) L and D = sum_t dO O, so that its softmax weights are the
+# final ones, and returns the step's contribution to the source rank's dK
+# and dV (what the reduce-scatter sums on that rank).
+
+def step_attention_bwd(q_r, k_src, v_src, dout_r, lse_r, delta_r, mode, scale=None):
+    """One step's part of a rank's backward, on local blocks of 2c rows.
+
+    q_r, dout_r [b, 2c, hq, d]; k_src, v_src [b, 2c, hkv, d]; lse_r, delta_r
+    [b, hq, 2c] the rank's final L and D.  Rows and keys as in
+    ``step_attention``.  Returns (dq [b, 2c, hq, d], zero outside the mode's
+    rows; dk, dv [b, 2c, hkv, d], the step's share of the source rank's
+    gradients).  For each head h of group g and row i of the mode:
+        P_j = exp(scale q_i.k_j - L_i),  dS_j = P_j (dO_i.v_j - D_i),
+        dq_i += scale sum_j dS_j k_j,  dk_j += scale dS_j q_i,  dv_j += P_j dO_i.
+    """
+    q_r, k_src, v_src, dout_r = (np.asarray(x, np.float64) for x in (q_r, k_src, v_src, dout_r))
+    b, two_c, hq, d = q_r.shape
+    hkv = k_src.shape[2]
+    group = hq // hkv
+    c = two_c // 2
+    if scale is None:
+        scale = default_scale(d)
+    if mode == CAUSAL:
+        rows, nkeys = np.arange(two_c), two_c
+    elif mode == KV_FIRST_HALF:
+        rows, nkeys = np.arange(two_c), c
+    elif mode == Q_SECOND_HALF:
+        rows, nkeys = np.arange(c, two_c), two_c
+    else:
+        raise ValueError("unknown mode")
+    visible = np.ones((len(rows), nkeys), bool)
+    if mode == CAUSAL:
+        visible = np.arange(nkeys)[None, :] <= rows[:, None]
+    dq = np.zeros_like(q_r)
+    dk = np.zeros((b, two_c, hkv, d))
+    dv = np.zeros((b, two_c, hkv, d))
+    for n in range(b):
+        for h in range(hq):
+            g = h // group
+            qh = q_r[n, rows, h]                      # [rows, d]
+            kh = k_src[n, :nkeys, g]                  # [keys, d]
+            vh = v_src[n, :nkeys, g]
+            doh = dout_r[n, rows, h]
+            z = scale * (qh @ kh.T)
+            p = np.where(visible, np.exp(z - lse_r[n, h, rows][:, None]), 0.0)
+            dp = doh @ vh.T
+            ds = p * (dp - delta_r[n, h, rows][:, None])
+            dq[n, rows, h] += scale * (ds @ kh)
+            dk[n, :nkeys, g] += scale * (ds.T @ qh)
+            dv[n, :nkeys, g] += p.T @ doh
+    return dq, dk, dv
+
+
+def cp_backward_rank(q, k, v, dout, cp, rank, scale=None, ring=step_schedule, nthreads=0):
+    """One rank's CP backward (no RoPE).
+
+    q, dout [b, s, hq, d]; k, v [b, s, hkv, d] unpartitioned.  The rank's O
+    and L come from ``cp_forward_rank``; D = sum_t dO O per row and head.
+    Returns (dq_r [b, 2c, hq, d], dkz, dvz [cp, b, 2c, hkv, d]): the rank's
+    query gradient and its contribution to every rank's K/V gradient.
+    """
+    s = q.shape[1]
+    qz, kz, vz, dz = (partition(x, cp) for x in (q, k, v, dout))
+    o_r, lse_r, _ = cp_forward_rank(q, k, v, cp, rank, scale, nthreads=nthreads)
+    delta_r = np.transpose(np.sum(np.asarray(dz[rank], np.float64) * o_r, axis=-1), (0, 2, 1))
+    dq_r = np.zeros(qz[rank].shape)
+    dkz = np.zeros(kz.shape)
+    dvz = np.zeros(vz.shape)
+    for i in range(cp):
+        mode, src = ring(i, rank, cp)
+        dq, dk, dv = step_attention_bwd(qz[rank], kz[src], vz[src], dz[rank], lse_r, delta_r,
+                                        mode, scale)
+        dq_r += dq
+        dkz[src] += dk
+        dvz[src] += dv
+    del s
+    return dq_r, dkz, dvz

@@ -10,7 +10,8 @@ warm-up steps, then K timed steps bracketed by synchronisation.
 The same share is also timed through the fused form (the split, then one
 cpattn_forward_fused launch that carries the online softmax across the cp
 key blocks, so there are no partials and no merge) and reported under
-"fused".
+"fused", and its backward (cpattn_backward with a seeded bf16 dO and the
+forward's merged O and L) under "backward".
 
 value = causal-effective FLOPs of the rank's share (4*d per visible query/
 key pair) / the measured time of a step.  Per-kernel times come from HIP
@@ -176,6 +177,28 @@ def main():
         fused = {"ms": float(np.mean([a.elapsed_time(b) for a, b in f_total])),
                  "attn_ms": float(np.mean([a.elapsed_time(b) for a, b in f_attn]))}
 
+    # the backward of the same share: dO seeded bf16, the rank's merged O
+    # and L from the forward above
+    backward = None
+    if w.dtype == "bf16":
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(99)
+        do_r = torch.randn(buf["o"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+        grads = P.alloc_grads(rank)
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                P.backward(grads, buf["o"], buf["lse"], do_r, stream)
+            torch.cuda.synchronize()
+            b_ev = []
+            for _ in range(args.steps):
+                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record(stream)
+                P.backward(grads, buf["o"], buf["lse"], do_r, stream)
+                e1.record(stream)
+                b_ev.append((e0, e1))
+            torch.cuda.synchronize()
+        backward = float(np.mean([a.elapsed_time(b) for a, b in b_ev]))
+
     # per-kernel times (ms) from the events, averaged over the timed steps
     part_ms, merge_ms, step_ms, total_ms = [], [], [[] for _ in range(w.cp)], []
     for evs in all_evs:
@@ -246,6 +269,17 @@ def main():
             "achieved": round(f_tf, 2),
             "frac": round(f_tf / peak, 4),
             "traffic": committed_traffic(w.name, "fused_traffic_bytes_per_launch"),
+        }
+    if backward is not None:
+        b_flops = 2.5 * flops
+        b_tf = b_flops / (backward * 1e-3) / 1e12
+        line["backward"] = {
+            "entry_point": "cpattn_backward",
+            "ms_per_step": round(backward, 4),
+            "flops": b_flops,
+            "flops_convention": "10*d per visible (q, k) pair: S, dP, dV, dK, dQ",
+            "value": round(b_tf, 2),
+            "frac": round(b_tf / peak, 4),
         }
     if args.cpu_sample_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, rank, args.cpu_sample_seconds)

@@ -185,6 +185,47 @@ int cpattn_forward_fused(const cpattn_dims *dims, int dtype, float scale, int ra
                          const void *qz, const void *kz, const void *vz, int out_dtype,
                          void *o_out, float *lse_out, void *stream);
 
+/* Backward, step by step.  The pages name the backward only through the
+ * communication context parallelism adds ("超大规模集群…", "CP 与其他技术结合":
+ * an all-gather of K/V and a reduce-scatter of their gradients); each ring
+ * step of the forward ("Megatron-LM 篇" 3.4: the three modes) has a
+ * backward counterpart on the same blocks that uses the rank's FINAL L
+ * (the merged lse_out of the forward) and D = sum_t dO O.
+ *
+ * cpattn_bwd_delta, device: delta_r [b, hq, 2c] fp32 = sum over the head
+ * dim of do_r [b, 2c, hq, d] (bf16) times o_r [b, 2c, hq, d] (fp32, the
+ * merged forward output).  d = 128. */
+int cpattn_bwd_delta(const cpattn_dims *dims, const float *o_r, const void *do_r,
+                     float *delta_r, void *stream);
+
+/* cpattn_step_bwd, device: one step's backward (CPATTN_BF16 only, d = 128).
+ * q_r, do_r [b, 2c, hq, d] bf16; k_src, v_src [b, 2c, hkv, d] bf16 (rank
+ * src's blocks); lse_r, delta_r [b, hq, 2c] fp32.  For each row i and head h
+ * of the mode and each key j it lets them see, with P = exp(scale q.k - L)
+ * and dS = P (dO.v - D):
+ *   dq_r [b, 2c, hq, d]  += scale * sum_j dS k_j      (fp32, rows of the mode)
+ *   dk_src [b, 2c, hkv, d] += scale * sum dS q_i      (fp32, summed over the
+ *   dv_src [b, 2c, hkv, d] += sum P dO_i               group's heads)
+ * The three gradient buffers accumulate: the caller zeroes them first. */
+int cpattn_step_bwd(const cpattn_dims *dims, int dtype, float scale, int mode,
+                    const void *q_r, const void *k_src, const void *v_src,
+                    const void *do_r, const float *lse_r, const float *delta_r,
+                    float *dq_r, float *dk_src, float *dv_src, void *stream);
+
+/* cpattn_backward, device: one rank's whole backward share.  Zeroes dq_r
+ * [b, 2c, hq, d], dkz and dvz [cp, b, 2c, hkv, d] (fp32), computes delta
+ * into delta_ws [b, hq, 2c] (caller's workspace), then the cp steps of
+ * cpattn_step_mode; step i adds to rank src's slices of dkz/dvz.  dkz/dvz
+ * hold the rank's contributions to every rank's K/V gradient: the inputs
+ * of the reduce-scatter that sums them on their owners.  qz, kz, vz:
+ * partitioned [cp, b, 2c, h, d] bf16; o_r, lse_r: the rank's merged forward
+ * output (fp32) and L; do_r [b, 2c, hq, d] bf16.  No RoPE (gradients are
+ * with respect to the rotated Q and K). */
+int cpattn_backward(const cpattn_dims *dims, int dtype, float scale, int rank,
+                    const void *qz, const void *kz, const void *vz, const float *o_r,
+                    const void *do_r, const float *lse_r, float *delta_ws, float *dq_r,
+                    float *dkz, float *dvz, void *stream);
+
 /* Static name of a status code. */
 const char *cpattn_status_str(int status);
 

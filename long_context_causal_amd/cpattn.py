@@ -71,11 +71,15 @@ def lib():
         L.cpattn_forward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, ctypes.c_size_t,
                                      I, P, P, P]
         L.cpattn_forward_fused.argtypes = [D, I, ctypes.c_float, I, P, P, P, I, P, P, P]
+        L.cpattn_bwd_delta.argtypes = [D, P, P, P, P]
+        L.cpattn_step_bwd.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P]
+        L.cpattn_backward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P, P]
         L.cpattn_status_str.argtypes = [I]
         L.cpattn_status_str.restype = ctypes.c_char_p
         for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
                      "cpattn_step_fwd", "cpattn_merge", "cpattn_forward",
-                     "cpattn_forward_fused"):
+                     "cpattn_forward_fused", "cpattn_bwd_delta", "cpattn_step_bwd",
+                     "cpattn_backward"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -167,3 +171,24 @@ def cpattn_forward_fused(dims, dtype, scale, rank, qz, kz, vz, out_dtype, o_out,
                                       _ptr(kz), _ptr(vz), out_dtype, _ptr(o_out), _ptr(lse_out),
                                       _stream(stream)),
            "cpattn_forward_fused")
+
+
+def cpattn_bwd_delta(dims, o_r, do_r, delta_r, stream=None):
+    _check(lib().cpattn_bwd_delta(ctypes.byref(dims), _ptr(o_r), _ptr(do_r), _ptr(delta_r),
+                                  _stream(stream)), "cpattn_bwd_delta")
+
+
+def cpattn_step_bwd(dims, dtype, scale, mode, q_r, k_src, v_src, do_r, lse_r, delta_r, dq_r,
+                    dk_src, dv_src, stream=None):
+    _check(lib().cpattn_step_bwd(ctypes.byref(dims), dtype, float(scale), mode, _ptr(q_r),
+                                 _ptr(k_src), _ptr(v_src), _ptr(do_r), _ptr(lse_r),
+                                 _ptr(delta_r), _ptr(dq_r), _ptr(dk_src), _ptr(dv_src),
+                                 _stream(stream)), "cpattn_step_bwd")
+
+
+def cpattn_backward(dims, dtype, scale, rank, qz, kz, vz, o_r, do_r, lse_r, delta_ws, dq_r, dkz,
+                    dvz, stream=None):
+    _check(lib().cpattn_backward(ctypes.byref(dims), dtype, float(scale), rank, _ptr(qz),
+                                 _ptr(kz), _ptr(vz), _ptr(o_r), _ptr(do_r), _ptr(lse_r),
+                                 _ptr(delta_ws), _ptr(dq_r), _ptr(dkz), _ptr(dvz),
+                                 _stream(stream)), "cpattn_backward")

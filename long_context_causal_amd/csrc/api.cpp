@@ -263,4 +263,75 @@ int cpattn_forward_fused(const cpattn_dims *dims, int dtype, float scale, int ra
     return e == hipSuccess ? CPATTN_OK : CPATTN_EHIP;
 }
 
+int cpattn_bwd_delta(const cpattn_dims *dims, const float *o_r, const void *do_r,
+                     float *delta_r, void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (!o_r || !do_r || !delta_r) return CPATTN_EINVAL;
+    if (dims->d != 128) return CPATTN_ESHAPE;
+    if (!aligned16(o_r) || !aligned16(do_r) || ((uintptr_t)delta_r & 3u)) return CPATTN_EALIGN;
+    const int64_t two_c = dims->s / dims->cp;
+    return status_of(cpattn::launch_bwd_delta(dims->b, two_c, dims->hq, o_r, do_r, delta_r,
+                                              (hipStream_t)stream));
+}
+
+int cpattn_step_bwd(const cpattn_dims *dims, int dtype, float scale, int mode, const void *q_r,
+                    const void *k_src, const void *v_src, const void *do_r, const float *lse_r,
+                    const float *delta_r, float *dq_r, float *dk_src, float *dv_src,
+                    void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (mode < CPATTN_CAUSAL || mode > CPATTN_Q_SECOND_HALF) return CPATTN_EINVAL;
+    if (!q_r || !k_src || !v_src || !do_r || !lse_r || !delta_r || !dq_r || !dk_src || !dv_src)
+        return CPATTN_EINVAL;
+    if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if (dims->d != 128) return CPATTN_ESHAPE;
+    if (!aligned16(q_r) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(do_r) ||
+        !aligned16(dq_r) || !aligned16(dk_src) || !aligned16(dv_src) ||
+        ((uintptr_t)lse_r & 3u) || ((uintptr_t)delta_r & 3u))
+        return CPATTN_EALIGN;
+    const StepGeom g = cpattn::step_geom(*dims, mode, scale);
+    return status_of(cpattn::launch_step_bwd_bf16(g, q_r, k_src, v_src, do_r, lse_r, delta_r,
+                                                  dq_r, dk_src, dv_src, (hipStream_t)stream));
+}
+
+int cpattn_backward(const cpattn_dims *dims, int dtype, float scale, int rank, const void *qz,
+                    const void *kz, const void *vz, const float *o_r, const void *do_r,
+                    const float *lse_r, float *delta_ws, float *dq_r, float *dkz, float *dvz,
+                    void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (rank < 0 || rank >= dims->cp) return CPATTN_EINVAL;
+    if (!qz || !kz || !vz || !o_r || !do_r || !lse_r || !delta_ws || !dq_r || !dkz || !dvz)
+        return CPATTN_EINVAL;
+    if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if (dims->d != 128) return CPATTN_ESHAPE;
+    if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz) || !aligned16(o_r) ||
+        !aligned16(do_r) || !aligned16(dq_r) || !aligned16(dkz) || !aligned16(dvz) ||
+        ((uintptr_t)lse_r & 3u) || ((uintptr_t)delta_ws & 3u))
+        return CPATTN_EALIGN;
+    const hipStream_t s = (hipStream_t)stream;
+    const int64_t two_c = dims->s / dims->cp;
+    const int64_t q_elems = dims->b * two_c * dims->hq * dims->d;
+    const int64_t kv_elems = dims->b * two_c * dims->hkv * dims->d;
+    const char *q_r = (const char *)qz + rank * q_elems * 2;
+    hipError_t e = cpattn::launch_fill_zero(dq_r, q_elems, s);
+    if (e == hipSuccess) e = cpattn::launch_fill_zero(dkz, kv_elems * dims->cp, s);
+    if (e == hipSuccess) e = cpattn::launch_fill_zero(dvz, kv_elems * dims->cp, s);
+    if (e == hipSuccess) e = cpattn::launch_bwd_delta(dims->b, two_c, dims->hq, o_r, do_r,
+                                                      delta_ws, s);
+    if (e != hipSuccess) return CPATTN_EHIP;
+    for (int i = 0; i < dims->cp; ++i) {
+        int mode, src;
+        cpattn_step_mode(i, rank, dims->cp, &mode, &src);
+        // ring hand-off: step i reads rank src's K/V and adds to src's dK/dV
+        const char *k_src = (const char *)kz + src * kv_elems * 2;
+        const char *v_src = (const char *)vz + src * kv_elems * 2;
+        st = cpattn_step_bwd(dims, dtype, scale, mode, q_r, k_src, v_src, do_r, lse_r,
+                             delta_ws, dq_r, dkz + src * kv_elems, dvz + src * kv_elems, stream);
+        if (st) return st;
+    }
+    return CPATTN_OK;
+}
+
 }  // extern "C"

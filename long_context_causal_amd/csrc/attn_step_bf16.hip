@@ -66,19 +66,14 @@
 // LDS reads are ordinary loads and transposing-read builtins the compiler
 // schedules.
 #include "internal.h"
+#include "mfma_tiles.h"
 
 #include <math.h>
 
 namespace cpattn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
+using namespace tiles;
 
 constexpr int D = 128;
 constexpr int BN = 64;                 // keys per LDS tile
@@ -190,36 +185,12 @@ struct FusedPlan {
     }
 };
 
-__device__ __forceinline__ int swap_bits23(int m) {
-    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-
-// K operand of one k-step for one 32-key half: the lane's 16-byte chunk.
-__device__ __forceinline__ bf16x8 k_read(unsigned addr) {
-    return __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)(uintptr_t)addr);
-}
-
-// V^T operand of key chunk kc (16 keys) for one 32-wide head-dim tile.  Lane
-// L = 16*g + 4*j + q reads, for s in {0, 1}, the 8-byte block at V row
-// kc*16 + 8*(g/2) + 4*s + j, head dims dt*32 + 16*(g%2) + 4*q .. +3; the
-// transpose hands lane t of group g the column dt*32 + 16*(g%2) + t for keys
-// +0..3 of that row block.  addr: row 8*(g/2) + j of the tile's dims block.
-__device__ __forceinline__ bf16x8 vt_read(unsigned addr) {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)addr);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4 *)(uintptr_t)(addr + 4 * ROWB));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // One direct global -> LDS copy of 16 bytes per lane from base + off (base

@@ -47,6 +47,19 @@ hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
                              const void *vz, void *o, bool out_bf16, float *lse,
                              hipStream_t stream);
 
+// Backward of one step (bf16, d = 128): dq += , dk += , dv += (fp32).
+hipError_t launch_step_bwd_bf16(const StepGeom &g, const void *q, const void *k,
+                                const void *v, const void *dout, const float *lse,
+                                const float *delta, float *dq, float *dk, float *dv,
+                                hipStream_t stream);
+
+// delta[n, h, i] = sum_t dout[n, i, h, t] o[n, i, h, t]; o fp32, dout bf16.
+hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o,
+                            const void *dout, float *delta, hipStream_t stream);
+
+// x[0 .. n) = 0 (n a multiple of 4, x 16-byte aligned).
+hipError_t launch_fill_zero(float *x, int64_t n, hipStream_t stream);
+
 hipError_t launch_step_f32(const StepGeom &g, const void *q, const void *k,
                            const void *v, float *o, float *lse,
                            hipStream_t stream);

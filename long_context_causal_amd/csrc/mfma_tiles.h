@@ -1,0 +1,54 @@
+// Operand tiles of v_mfma_f32_32x32x16_bf16 on gfx950: vector types, the
+// row permutation that makes an MFMA result the next MFMA's operand, and
+// the two LDS reads that feed the matrix cores.  Shared by the forward and
+// backward attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+namespace tiles {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Matrix row m of an MFMA operand is fed tile row swap_bits23(m) (bits 2 and
+// 3 swapped): then register v of a 32x32 result, which holds matrix row
+// 8*(v/4) + 4*hi + v%4, holds tile row 8*hi + v (v < 8) or 16 + 8*hi + v-8,
+// i.e. the 8 consecutive rows a lane supplies along K of the next MFMA.
+__device__ __forceinline__ inline int swap_bits23(int m) {
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Bytes of one LDS tile row: a bf16 row of a 128-wide head.
+constexpr int ROW_BYTES = 256;
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Row operand of one k-step (16 consecutive head dims of one tile row): the
+// lane's 16-byte chunk, one ds_read_b128.
+__device__ __forceinline__ inline bf16x8 k_read(unsigned addr) {
+    return __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)(uintptr_t)addr);
+}
+
+// Transposed operand (8 consecutive tile rows of one head-dim column per
+// lane) of row chunk kc (16 rows) for one 32-wide head-dim tile.  Lane
+// L = 16*g + 4*j + q reads, for s in {0, 1}, the 8-byte block at tile row
+// kc*16 + 8*(g/2) + 4*s + j, head dims dt*32 + 16*(g%2) + 4*q .. +3; the
+// transpose hands lane t of group g the column dt*32 + 16*(g%2) + t for rows
+// +0..3 of that row block.  addr: row 8*(g/2) + j of the tile's dims block.
+__device__ __forceinline__ inline bf16x8 vt_read(unsigned addr) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)addr);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)(uintptr_t)(addr + 4 * ROW_BYTES));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace tiles
+}  // namespace cpattn

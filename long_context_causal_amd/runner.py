@@ -120,6 +120,23 @@ class CPProblem:
                                self.vz, out["out_dtype"], out["o"],
                                out["lse"] if with_lse else None, stream)
 
+    # --- backward of one rank's share ------------------------------------------
+    def alloc_grads(self, rank):
+        """Gradient buffers of ``rank``'s backward share (fp32)."""
+        two_c = 2 * self.c
+        f = dict(dtype=torch.float32, device=self.device)
+        return dict(rank=rank,
+                    delta=torch.empty((self.b, self.w.hq, two_c), **f),
+                    dq=torch.empty((self.b, two_c, self.w.hq, self.w.d), **f),
+                    dkz=torch.empty((self.cp, self.b, two_c, self.w.hkv, self.w.d), **f),
+                    dvz=torch.empty((self.cp, self.b, two_c, self.w.hkv, self.w.d), **f))
+
+    def backward(self, grads, o_r, lse_r, do_r, stream=None, scale=0.0):
+        """The rank's backward share through cpattn_backward."""
+        C.cpattn_backward(self.dims, self.dtype, scale, grads["rank"], self.qz, self.kz,
+                          self.vz, o_r, do_r, lse_r, grads["delta"], grads["dq"], grads["dkz"],
+                          grads["dvz"], stream)
+
 
 def _round256(x):
     return (x + 255) // 256 * 256

@@ -1,0 +1,145 @@
+"""GPU backward of the CP scheme (cpattn_step_bwd, cpattn_backward) vs the
+backward oracle.
+
+* every step mode through cpattn_step_bwd, with the oracle's final L and D
+  as inputs, vs the oracle's step backward (dq, dk, dv contributions);
+* every rank's whole backward share at reduced length (GQA, MHA with wide
+  logits, RoPE, ragged tiles): the ranks' dK/dV contributions summed per
+  owner (the reduce-scatter) and every rank's dQ, un-permuted, vs the
+  non-CP gradients.  The GPU's own forward output and L feed its backward;
+* the headline workload at full size: dQ of sampled rows of the measured
+  rank vs the oracle.
+
+Bound (bf16 rounding of P and dS in the products, 2^-9 relative per term;
+gradients are sums with cancellation, so the error is measured against
+the gradient's own scale): max |err| <= 1e-2 * max |ref| and mean |err|
+<= 5e-3 * mean |ref|, per gradient.
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import (C, CPProblem, as_f32, make_inputs, ocp, say, small, to_device, torch)
+from long_context_causal_amd.inputs import WORKLOADS, f32_to_bf16_bits
+from oracle import attention_rows, attention_rows_bwd, causal_attention_bwd
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, MEAN_REL = 1e-2, 5e-3
+
+
+def assert_grad(name, got, ref):
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    mx, mn = err.max(), err.mean()
+    rmx, rmn = np.abs(ref).max(), np.abs(ref).mean()
+    say(f"  [{name}] max_err={mx:.3e} ({mx / rmx:.2e} of max|ref|) "
+        f"mean_err={mn:.3e} ({mn / rmn:.2e} of mean|ref|)")
+    assert mx <= MAX_REL * rmx, f"{name}: max error {mx} > {MAX_REL} * {rmx}"
+    assert mn <= MEAN_REL * rmn, f"{name}: mean error {mn} > {MEAN_REL} * {rmn}"
+
+
+def _dout(w, seed=99):
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.standard_normal((w.b, w.s, w.hq, w.d)).astype(np.float32))
+
+
+def _rotated(w, q, k):
+    qf, kf = as_f32(q).astype(np.float64), as_f32(k).astype(np.float64)
+    if w.rope_theta is not None:
+        ar = np.arange(w.s)
+        qf, kf = ocp.rope(qf, ar, w.rope_theta), ocp.rope(kf, ar, w.rope_theta)
+    return qf, kf
+
+
+REDUCED = [("bf16_gqa_s32k_cp8", 2 * 8 * 64), ("bf16_gqa_s8k_cp4", 2 * 4 * 100),
+           ("bf16_mha_s16k_cp4_widelogits", 2 * 4 * 96), ("bf16_gqa_s128k_cp16_rope", 2 * 16 * 24)]
+
+
+@pytest.mark.parametrize("name,s", REDUCED)
+def test_backward_all_ranks_reduced(name, s):
+    w = small(WORKLOADS[name], s)
+    say(f"backward reduced {name} s={s}")
+    q, k, v = make_inputs(w)
+    do = _dout(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    doz = ocp.partition(as_f32(do), w.cp)
+    two_c = 2 * w.c
+    dq_z = np.zeros((w.cp, w.b, two_c, w.hq, w.d))
+    dk_z = np.zeros((w.cp, w.b, two_c, w.hkv, w.d))
+    dv_z = np.zeros_like(dk_z)
+    for r in range(w.cp):
+        buf = P.alloc_rank(r, C.CPATTN_F32)
+        P.forward(buf)
+        g = P.alloc_grads(r)
+        P.backward(g, buf["o"], buf["lse"], to_device(f32_to_bf16_bits(doz[r].astype(np.float32))))
+        torch.cuda.synchronize()
+        dq_z[r] = g["dq"].cpu().numpy()
+        dk_z += g["dkz"].cpu().numpy()        # the reduce-scatter, summed on the owner
+        dv_z += g["dvz"].cpu().numpy()
+    qf, kf = _rotated(w, q, k)
+    dq, dk, dv = causal_attention_bwd(qf, kf, as_f32(v).astype(np.float64),
+                                      as_f32(do).astype(np.float64))
+    assert_grad("dQ", ocp.unpartition(dq_z, w.s), dq)
+    assert_grad("dK", ocp.unpartition(dk_z, w.s), dk)
+    assert_grad("dV", ocp.unpartition(dv_z, w.s), dv)
+
+
+@pytest.mark.parametrize("mode", [C.CPATTN_CAUSAL, C.CPATTN_KV_FIRST_HALF, C.CPATTN_Q_SECOND_HALF])
+def test_step_bwd_each_mode(mode):
+    w = small(WORKLOADS["bf16_gqa_s8k_cp4"], 2 * 4 * 72)
+    say(f"step backward mode {ocp.MODE_NAMES[mode]}")
+    rng = np.random.default_rng(7 + mode)
+    two_c, c = 2 * w.c, w.c
+    shp_q, shp_k = (w.b, two_c, w.hq, w.d), (w.b, two_c, w.hkv, w.d)
+    q, do = (f32_to_bf16_bits((rng.standard_normal(shp_q) * 0.5).astype(np.float32)) for _ in range(2))
+    k, v = (f32_to_bf16_bits((rng.standard_normal(shp_k) * 0.5).astype(np.float32)) for _ in range(2))
+    qf, kf, vf, dof = (as_f32(x).astype(np.float64) for x in (q, k, v, do))
+    # the rank's "final" L and D, from the oracle: here the whole local block
+    # causally (any L and D the kernel is given must be used as given)
+    o_ref, lse = attention_rows(qf, kf, vf, np.arange(1, two_c + 1))
+    delta = np.transpose(np.sum(dof * o_ref, axis=-1), (0, 2, 1))
+    dq_ref, dk_ref, dv_ref = ocp.step_attention_bwd(qf, kf, vf, dof, lse, delta, mode)
+    dims = C.make_dims(w.b, w.s, w.hq, w.hkv, w.d, w.cp)
+    dq = torch.zeros(shp_q, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(shp_k, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(shp_k, dtype=torch.float32, device="cuda")
+    C.cpattn_step_bwd(dims, C.CPATTN_BF16, 0.0, mode, to_device(q), to_device(k), to_device(v),
+                      to_device(do), to_device(lse.astype(np.float32)),
+                      to_device(delta.astype(np.float32)), dq, dk, dv)
+    torch.cuda.synchronize()
+    rows = slice(c, two_c) if mode == C.CPATTN_Q_SECOND_HALF else slice(0, two_c)
+    assert_grad("dQ", dq.cpu().numpy()[:, rows], dq_ref[:, rows])
+    keys = slice(0, c) if mode == C.CPATTN_KV_FIRST_HALF else slice(0, two_c)
+    assert_grad("dK", dk.cpu().numpy()[:, keys], dk_ref[:, keys])
+    assert_grad("dV", dv.cpu().numpy()[:, keys], dv_ref[:, keys])
+    # rows and keys outside the mode are left untouched (still zero)
+    assert not dq.cpu().numpy()[:, : (c if mode == C.CPATTN_Q_SECOND_HALF else 0)].any()
+    assert not dk.cpu().numpy()[:, (c if mode == C.CPATTN_KV_FIRST_HALF else two_c):].any()
+
+
+def test_backward_full_size_sampled_dq():
+    w = WORKLOADS["bf16_gqa_s32k_cp8"]
+    r = w.rank
+    say(f"backward full {w.name}: rank {r}")
+    q, k, v = make_inputs(w)
+    do = _dout(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    doz_r = ocp.partition(as_f32(do), w.cp)[r]
+    buf = P.alloc_rank(r, C.CPATTN_F32)
+    P.forward(buf)
+    g = P.alloc_grads(r)
+    P.backward(g, buf["o"], buf["lse"], to_device(f32_to_bf16_bits(doz_r.astype(np.float32))))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, w.c - 1, w.c, 2 * w.c - 1],
+                                     rng.choice(2 * w.c, 6, replace=False)]))
+    pos = ocp.zigzag_positions(w.s, w.cp, r)[rows]
+    hi = int(pos.max()) + 1
+    qf = as_f32(q[:, pos]).astype(np.float64)
+    dof = as_f32(do[:, pos]).astype(np.float64)
+    kf, vf = (as_f32(x[:, :hi]).astype(np.float64) for x in (k, v))
+    say(f"  oracle on {len(rows)} rows")
+    dq_ref, _, _ = attention_rows_bwd(qf, kf, vf, dof, pos + 1)
+    assert_grad("dQ rows", g["dq"].cpu().numpy()[:, rows], dq_ref)

@@ -60,7 +60,7 @@ struct BwdParams {
     const float *lse, *delta;           // the rank's final L (natural log) and D [b, hq, 2c]
     float *dq, *dk, *dv;                // accumulated: dq [b, 2c, hq, d]; dk, dv [b, 2c, hkv, d]
     int64_t two_c, q_row0;
-    int nq, nk, hq, hkv, group, ntiles_wg;
+    int b, nq, nk, hq, hkv, group, ntiles_wg, head_splits;
     float scale, scale_log2;
     int causal;
 };
@@ -227,80 +227,90 @@ attn_bwd_dq(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 4 waves x 32 keys of one (batch, KV head); streams
-// 32-row tiles of Q and dO (R and T layouts) and their L and D, for every
-// query head of the group, double-buffered in LDS.
-__global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// dK, dV: workgroup = 8 waves on 128 keys of one (batch, KV head).  Waves
+// 0-3 ("P waves") own 32 keys each with K as B operand: S = Q K^T, P, and
+// dV^T += dO^T P; each hands its fp32 P to LDS.  Waves 4-7 ("dS waves") own
+// the same keys with V as B operand and run one tile behind: dP = dO V^T,
+// dS = P (dP - D) with the P handed over, dK^T += Q^T dS.  Every product is
+// computed once, and each wave fits in half the register file, so the two
+// waves of a key group share a SIMD and overlap their vector and matrix work.
+// The workgroup streams 32-row tiles of Q and dO (with L and D) for hpw
+// query heads of the group; the group's heads are split over head_splits
+// workgroups, which sum into dk, dv with fp32 atomics.
+constexpr int NWK = 8;                         // waves per dK/dV workgroup
+constexpr int KW = 4;                          // key groups of 32 per workgroup
+constexpr int TBUF = 4 * TB + 2 * TR * 4;      // one tile: Q R, Q T, dO R, dO T, L, D
+constexpr int PSLAB = 64 * 16 * 4;             // one key group's fp32 P of a tile
+constexpr int DKDV_LDS = 3 * TBUF + 2 * KW * PSLAB;
+
+__global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv(BwdParams p) {
-    constexpr int BUF = 4 * TB + 2 * TR * 4;   // Q R, Q T, dO R, dO T, L, D
-    __shared__ __attribute__((aligned(1024))) char lds[2 * BUF];
+    __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool ds_wave = wave >= KW;           // wave-uniform role
+    const int kwave = wave & (KW - 1);
     const int hi = lane >> 5, l32 = lane & 31;
+    // longest (causal: first) key blocks are dispatched first
     int item = blockIdx.x;
-    const int nkt = p.ntiles_wg;
-    const int kt = item % nkt;                 // causal: early key tiles see the most rows
-    item /= nkt;
+    const int inner = p.head_splits * p.hkv * p.b;
+    const int kt = item / inner;
+    item %= inner;
+    const int hs = item % p.head_splits;
+    item /= p.head_splits;
     const int g = item % p.hkv;
     const int n = item / p.hkv;
-    const int k0 = kt * TR * NWB;
-    const int wkey0 = k0 + wave * TR;
+    const int hpw = p.group / p.head_splits;   // query heads of this workgroup
+    const int h0 = g * p.group + hs * hpw;
+    const int k0 = kt * TR * KW;
+    const int wkey0 = k0 + kwave * TR;
 
     LaneOffsets L;
     L.init(lane);
     const unsigned lbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
+    float *pslab0 = (float *)(lds + 3 * TBUF + kwave * PSLAB);
 
-    // this lane's key: K and V as B operands of S = Q K^T and dP = dO V^T
+    // this lane's key: K (P waves) or V (dS waves) as B operands
     const int key = wkey0 + l32;
     const int kr = min(key, p.nk - 1);
     const int64_t koff = ((n * p.two_c + kr) * (int64_t)p.hkv + g) * D;
-    bf16x8 kf[D / 16], vf[D / 16];
-    load_b_rows(p.k + koff, hi, kf);
-    load_b_rows(p.v + koff, hi, vf);
-    f32x16 adk[D / 32], adv[D / 32];
+    bf16x8 bf[D / 16];
+    load_b_rows((ds_wave ? p.v : p.k) + koff, hi, bf);
+    f32x16 acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            adk[dt][e] = 0.0f;
-            adv[dt][e] = 0.0f;
-        }
+        for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
 
-    // query tiles: every head of the group, rows from the first one that can
-    // see this workgroup's keys (causal: row >= key) to the end
+    // query tiles: rows from the first one that can see this workgroup's
+    // keys (causal: row >= key) to the end, for each of the hpw heads
     const int qstart = p.causal ? (k0 / TR) : 0;
     const int nqt = (p.nq + TR - 1) / TR;
     const int per_head = max(nqt - qstart, 0);
-    const int ntiles = per_head * p.group;
-    u32x4 qreg[CPT], dreg[CPT];
+    const int ntiles = per_head * hpw;
+    u32x4 qreg, dreg;
     float lreg = 0.0f, dreg1 = 0.0f;
     auto gload = [&](int u) {
-        const int head = g * p.group + u / per_head;
+        const int head = h0 + u / per_head;
         const int qt = qstart + u % per_head;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int row = min(qt * TR + tile_row(tid, i), p.nq - 1);
-            const int64_t off = ((n * p.two_c + p.q_row0 + row) * (int64_t)p.hq + head) * D;
-            qreg[i] = *(const u32x4 *)(p.q + off + (tid & 15) * 8);
-            dreg[i] = *(const u32x4 *)(p.dout + off + (tid & 15) * 8);
-        }
+        const int row = min(qt * TR + tid / 16, p.nq - 1);
+        const int64_t off = ((n * p.two_c + p.q_row0 + row) * (int64_t)p.hq + head) * D;
+        qreg = *(const u32x4 *)(p.q + off + (tid & 15) * 8);
+        dreg = *(const u32x4 *)(p.dout + off + (tid & 15) * 8);
         if (tid < TR) {
-            const int row = min(qt * TR + tid, p.nq - 1);
-            const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + p.q_row0 + row;
+            const int lrow_q = min(qt * TR + tid, p.nq - 1);
+            const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + p.q_row0 + lrow_q;
             lreg = p.lse[lrow] * 1.4426950408889634f;
             dreg1 = p.delta[lrow];
         }
     };
     auto lstore = [&](int buf) {
-        char *base = lds + buf * BUF;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int r = tile_row(tid, i), c = tid & 15;
-            *(u32x4 *)(base + r_off(r, c)) = qreg[i];
-            *(u32x4 *)(base + TB + t_off(r, c)) = qreg[i];
-            *(u32x4 *)(base + 2 * TB + r_off(r, c)) = dreg[i];
-            *(u32x4 *)(base + 3 * TB + t_off(r, c)) = dreg[i];
-        }
+        char *base = lds + buf * TBUF;
+        const int r = tid / 16, c = tid & 15;
+        *(u32x4 *)(base + r_off(r, c)) = qreg;
+        *(u32x4 *)(base + TB + t_off(r, c)) = qreg;
+        *(u32x4 *)(base + 2 * TB + r_off(r, c)) = dreg;
+        *(u32x4 *)(base + 3 * TB + t_off(r, c)) = dreg;
         if (tid < TR) {
             ((float *)(base + 4 * TB))[tid] = lreg;
             ((float *)(base + 4 * TB + TR * 4))[tid] = dreg1;
@@ -311,72 +321,110 @@ attn_bwd_dkdv(BwdParams p) {
         lstore(0);
     }
     __syncthreads();
-    for (int u = 0; u < ntiles; ++u) {
-        if (u + 1 < ntiles) gload(u + 1);
-        const int qt = qstart + u % per_head;
-        const int q0 = qt * TR;
-        // the wave's keys are visible to some row of the tile
-        if (!p.causal || q0 + TR - 1 >= wkey0) {
-            const unsigned sQ = lbase + (u & 1) * BUF, sQT = sQ + TB, sD = sQ + 2 * TB,
-                           sDT = sQ + 3 * TB;
-            const char *lb = lds + (u & 1) * BUF + 4 * TB;
-            f32x16 s = {}, dp = {};
+    // iteration it: P waves on tile it, dS waves on tile it - 1; tile u sits
+    // in buffer u % 3 and its P in slab u % 2
+    int buf_p = 0, buf_ds = 2, buf_next = 1;
+    for (int it = 0; ntiles > 0 && it <= ntiles; ++it) {
+        if (it + 1 < ntiles) gload(it + 1);
+        const int u = ds_wave ? it - 1 : it;
+        const int q0 = (qstart + (u < 0 ? 0 : u) % per_head) * TR;
+        // the tile exists and some row of it sees the wave's keys
+        if (u >= 0 && u < ntiles && (!p.causal || q0 + TR - 1 >= wkey0)) {
+            const int buf = ds_wave ? buf_ds : buf_p;
+            const unsigned sT = lbase + buf * TBUF;
+            const char *lb = lds + buf * TBUF + 4 * TB;
+            float *slab = pslab0 + (u & 1) * (KW * PSLAB / 4);
+            bf16x8 ob[2];
+            if (!ds_wave) {
+                f32x16 s = {};
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                s = MFMA(k_read(sQ + L.roff[kk]), kf[kk], s, 0, 0, 0);
-                dp = MFMA(k_read(sD + L.roff[kk]), vf[kk], dp, 0, 0, 0);
-            }
-            bf16x8 pb[2], dsb[2];
+                for (int kk = 0; kk < D / 16; ++kk)
+                    s = MFMA(k_read(sT + L.roff[kk]), bf[kk], s, 0, 0, 0);
+                f32x16 pv;
 #pragma unroll
-            for (int qc = 0; qc < 2; ++qc) {
-                // L and D of the 8 rows this lane holds: 16*qc + 8*hi .. +7
-                const f32x8 lv = *(const f32x8 *)(lb + (16 * qc + 8 * hi) * 4);
-                const f32x8 dv8 = *(const f32x8 *)(lb + TR * 4 + (16 * qc + 8 * hi) * 4);
-                f32x8 pv, ds;
+                for (int qc = 0; qc < 2; ++qc) {
+                    const f32x8 lv = *(const f32x8 *)(lb + (16 * qc + 8 * hi) * 4);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int row = q0 + 16 * qc + 8 * hi + e;
-                    const bool vis = row < p.nq && key < p.nk && (!p.causal || key <= row);
-                    pv[e] = vis ? __builtin_amdgcn_exp2f(
+                    for (int e = 0; e < 8; ++e) {
+                        const int row = q0 + 16 * qc + 8 * hi + e;
+                        const bool vis = row < p.nq && key < p.nk && (!p.causal || key <= row);
+                        pv[qc * 8 + e] =
+                            vis ? __builtin_amdgcn_exp2f(
                                       __builtin_fmaf(s[qc * 8 + e], p.scale_log2, -lv[e]))
                                 : 0.0f;
-                    ds[e] = pv[e] * (dp[qc * 8 + e] - dv8[e]);
+                    }
                 }
-                pb[qc] = __builtin_convertvector(pv, bf16x8);
-                dsb[qc] = __builtin_convertvector(ds, bf16x8);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *(f32x4 *)(slab + (j * 64 + lane) * 4) =
+                        f32x4{pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]};
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc) {
+                    f32x8 h;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) h[e] = pv[qc * 8 + e];
+                    ob[qc] = __builtin_convertvector(h, bf16x8);
+                }
+            } else {
+                f32x16 dp = {};
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk)
+                    dp = MFMA(k_read(sT + 2 * TB + L.roff[kk]), bf[kk], dp, 0, 0, 0);
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc) {
+                    const f32x8 dv8 = *(const f32x8 *)(lb + TR * 4 + (16 * qc + 8 * hi) * 4);
+                    const f32x4 pa = *(const f32x4 *)(slab + ((2 * qc) * 64 + lane) * 4);
+                    const f32x4 pb = *(const f32x4 *)(slab + ((2 * qc + 1) * 64 + lane) * 4);
+                    f32x8 ds;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ds[e] = pa[e] * (dp[qc * 8 + e] - dv8[e]);
+                        ds[4 + e] = pb[e] * (dp[qc * 8 + 4 + e] - dv8[4 + e]);
+                    }
+                    ob[qc] = __builtin_convertvector(ds, bf16x8);
+                }
             }
+            // P waves: dV^T += dO^T P;  dS waves: dK^T += Q^T dS
+            const unsigned sA = sT + (ds_wave ? TB : 3 * TB);
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc)
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) {
-                    adv[dt] = MFMA(vt_read(sDT + L.toff[dt] + qc * 16 * RB), pb[qc], adv[dt], 0,
+                for (int dt = 0; dt < D / 32; ++dt)
+                    acc[dt] = MFMA(vt_read(sA + L.toff[dt] + qc * 16 * RB), ob[qc], acc[dt], 0,
                                    0, 0);
-                    adk[dt] = MFMA(vt_read(sQT + L.toff[dt] + qc * 16 * RB), dsb[qc], adk[dt],
-                                   0, 0, 0);
-                }
         }
-        if (u + 1 < ntiles) lstore((u + 1) & 1);
+        if (it + 1 < ntiles) lstore(buf_next);
         __syncthreads();
+        buf_ds = buf_p;
+        buf_p = buf_next;
+        buf_next = buf_next == 2 ? 0 : buf_next + 1;
     }
 
-    if (key < p.nk) {
-        float *dk = p.dk + koff + 4 * hi;
-        float *dv = p.dv + koff + 4 * hi;
+    // dv += dV (P waves), dk += scale dK (dS waves); lane holds head dims
+    // dt*32 + 8*i + 4*hi + j.  Split heads add with atomics.
+    if (key < p.nk && ntiles > 0) {
+        float *dst = (ds_wave ? p.dk : p.dv) + koff + 4 * hi;
+        const float f = ds_wave ? p.scale : 1.0f;
+        if (p.head_splits == 1) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 *a = (f32x4 *)(dk + dt * 32 + i * 8);
-                f32x4 *b = (f32x4 *)(dv + dt * 32 + i * 8);
-                f32x4 wa = *a, wb = *b;
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 *a = (f32x4 *)(dst + dt * 32 + i * 8);
+                    f32x4 w = *a;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    wa[j] += p.scale * adk[dt][i * 4 + j];
-                    wb[j] += adv[dt][i * 4 + j];
+                    for (int j = 0; j < 4; ++j) w[j] += f * acc[dt][i * 4 + j];
+                    *a = w;
                 }
-                *a = wa;
-                *b = wb;
-            }
+        } else {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        unsafeAtomicAdd(dst + dt * 32 + i * 8 + j, f * acc[dt][i * 4 + j]);
+        }
     }
 }
 
@@ -450,6 +498,7 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const void *q, const void *k,
     p.nk = (int)g.nk;
     p.hq = g.hq;
     p.hkv = g.hkv;
+    p.b = (int)g.b;
     p.group = g.hq / g.hkv;
     p.scale = g.scale;
     p.scale_log2 = g.scale_log2;
@@ -460,9 +509,16 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const void *q, const void *k,
                        dim3(64 * NWB), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    p.ntiles_wg = (int)((g.nk + rows_wg - 1) / rows_wg);
-    hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)((int64_t)p.ntiles_wg * g.hkv * g.b)),
-                       dim3(64 * NWB), 0, stream, p);
+    // key tiles of TR * KW keys; the group's heads split so the grid has
+    // at least ~2 workgroups per CU (heads per workgroup divides the group)
+    p.ntiles_wg = (int)((g.nk + TR * KW - 1) / (TR * KW));
+    const int64_t base_wgs = (int64_t)p.ntiles_wg * g.hkv * g.b;
+    p.head_splits = 1;
+    while (p.head_splits < p.group && p.group % (p.head_splits * 2) == 0 &&
+           base_wgs * p.head_splits < 512)
+        p.head_splits *= 2;
+    hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)(base_wgs * p.head_splits)),
+                       dim3(64 * NWK), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -32,11 +32,12 @@
 //
 // LDS: a streamed tile is contracted over the head dim (row chunks,
 // ds_read_b128) and over its rows (8 rows of one column per lane,
-// ds_read_b64_tr_b16), so the tiles that need both are written twice, in
-// two XOR swizzles: "R" (16-byte chunk c of row r at c ^ (swap_bits23(r) &
-// 15)) and "T" (at c ^ ((r & 3) << 2)); each keeps its read pattern free
-// of bank conflicts.  Tiles are double-buffered: the next tile's global
-// loads are in flight while the current one is computed; one barrier per
+// ds_read_b64_tr_b16).  One XOR swizzle keeps both reads free of bank
+// conflicts: 16-byte chunk c of tile row r sits at chunk c ^ u_swz(r), with
+// u_swz(r) = 4 (r % 4) + (r / 4) % 4.  Tiles are copied global -> LDS
+// directly (global_load_lds, no register round trip) several tiles ahead of
+// their use into a ring of stages; each lane copies fixed chunks, chosen so
+// that the copy's linear LDS order is the swizzled layout.  One barrier per
 // tile.  The MFMAs are compiler builtins, so the compiler pads every hazard.
 #include "internal.h"
 #include "mfma_tiles.h"
@@ -49,11 +50,10 @@ namespace {
 using namespace tiles;
 
 constexpr int D = 128;
-constexpr int NWB = 4;                     // waves per workgroup
 constexpr int TR = 32;                     // rows of a streamed tile; rows (keys) per wave
 constexpr int RB = ROW_BYTES;              // bytes per tile row
-constexpr int TB = TR * RB;                // bytes per tile in one layout
-constexpr int CPT = TR * (D / 8) / (64 * NWB);   // 16-byte chunks per thread per tile (= 2)
+constexpr int TB = TR * RB;                // bytes per tile
+constexpr float LOG2E = 1.4426950408889634f;
 
 struct BwdParams {
     const uint16_t *q, *k, *v, *dout;   // q_r, dout_r [b, 2c, hq, d]; k, v [b, 2c, hkv, d]
@@ -65,36 +65,55 @@ struct BwdParams {
     int causal;
 };
 
-// Byte offset of chunk c of tile row r in the two layouts.
-__device__ __forceinline__ unsigned r_off(int r, int c) {
-    return r * RB + ((c ^ (swap_bits23(r) & 15)) << 4);
-}
-__device__ __forceinline__ unsigned t_off(int r, int c) {
-    return r * RB + ((c ^ ((r & 3) << 2)) << 4);
-}
+__device__ __forceinline__ int u_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// The lane's offsets for the two reads (see the header): row operand of
-// k-step kk from an R tile, transposed operand of head-dim tile dt from a T
-// tile (plus kc * 16 * RB for the second 16-row chunk).
+// The lane's LDS byte offsets in a swizzled tile, kept as a few bases and
+// XOR masks (the swizzle is an XOR, so each offset is one v_xad):
+//   row operand of k-step kk (row r = swap_bits23(l32), chunk 2 kk + hi):
+//     r*RB + 32 ((kk ^ g)) + 16 (hi ^ (f & 1)),  f = u_swz(r), g = f >> 1;
+//   transposed read s of head-dim tile dt (row 8 (lane/32) + 4 s + j,
+//   chunk 4 dt + x, byte 8 (lane & 1)): tb[s] + 64 (dt ^ (f' >> 2)), where
+//   f' = u_swz(row) (rows +0 and +4 differ only in bit 0 of f');
+// add kc * 16 * RB for the second 16-row chunk, which has the same swizzle.
 struct LaneOffsets {
-    unsigned roff[D / 16];
-    unsigned toff[D / 32];
+    unsigned rbase, rmask, tb[2], tmask;
     __device__ __forceinline__ void init(int lane) {
         const int hi = lane >> 5, l32 = lane & 31;
         const int r = swap_bits23(l32);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) roff[kk] = r * RB + (((kk * 2 + hi) ^ (l32 & 15)) << 4);
+        const int f = u_swz(r);
+        rbase = r * RB + 16 * (hi ^ (f & 1));
+        rmask = (unsigned)(f >> 1) << 5;
         const int vg = lane >> 4, vj = (lane >> 2) & 3, vq = lane & 3;
         const int x = 2 * (vg & 1) + (vq >> 1);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-            toff[dt] = (8 * (vg >> 1) + vj) * RB + (((dt * 4 + x) ^ (vj << 2)) << 4) + (vq & 1) * 8;
+        for (int s = 0; s < 2; ++s) {
+            const int row = 8 * (vg >> 1) + 4 * s + vj;
+            tb[s] = row * RB + (((x ^ u_swz(row)) & 3) << 4) + (vq & 1) * 8;
+        }
+        tmask = (unsigned)(u_swz(8 * (vg >> 1) + vj) >> 2) << 6;
+    }
+    __device__ __forceinline__ unsigned roff(int kk) const { return ((kk << 5) ^ rmask) + rbase; }
+    __device__ __forceinline__ unsigned toff(int dt, int s) const {
+        return ((dt << 6) ^ tmask) + tb[s];
     }
 };
 
-// The 16-byte chunks a thread copies of a 32-row tile: rows tid/16 and
-// tid/16 + 16, chunk tid%16.
-__device__ __forceinline__ int tile_row(int tid, int i) { return tid / 16 + 16 * i; }
+// Transposed operand from two row blocks (see vt_read).
+__device__ __forceinline__ bf16x8 vt_read2(unsigned a0, unsigned a1) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)a1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Copy of 4 tile rows (1 KB: rows 4m .. 4m+3 of a tile, m the copy's index
+// in the tile) into the swizzled layout: lane L lands on row 4m + L/16,
+// chunk L%16, so it loads chunk (L%16) ^ u_swz(row) of that row.  Returns
+// the lane's byte offset from the copy's first row; u_swz(row) depends on m
+// only through m % 4.
+__device__ __forceinline__ unsigned copy_offset(int lane, int m, int64_t row_bytes) {
+    const int r = lane >> 4;
+    return (unsigned)(r * row_bytes) + ((((lane & 15) ^ ((r << 2) | (m & 3)))) << 4);
+}
 
 // B operand of the 8 k-steps for one row (this lane's l32-th row of a
 // 32-row block): row chunks kk*16 + 8*hi .. +7.
@@ -104,14 +123,50 @@ __device__ __forceinline__ void load_b_rows(const uint16_t *row, int hi, bf16x8 
         f[kk] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(row + kk * 16 + hi * 8));
 }
 
+// Makes the compiler wait for the load of x here, before the tile loop, so
+// that no wait for it is left inside the loop.
+template <class T>
+__device__ __forceinline__ void settle(const T &x) {
+    asm volatile("" ::"v"(x));
+}
+template <class T, int N>
+__device__ __forceinline__ void settle(const T (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) settle(x[i]);
+}
+
 #define MFMA __builtin_amdgcn_mfma_f32_32x32x16_bf16
+
+// Issues one wave's copies of rows [4 m, 4 m + 4) of a 32-row tile whose
+// first row is row0 (of n rows; rows past n repeat row n-1) from the row
+// array base (row stride row_bytes) into the stage tile at sdst.  off: the
+// lane's copy_offset for m.
+__device__ __forceinline__ void copy_rows(const uint16_t *base, int64_t row_bytes, int row0,
+                                          int n, int m, unsigned off, unsigned sdst, int lane) {
+    if (row0 + TR <= n) {
+        dma16((const char *)base + (row0 + 4 * m) * row_bytes, off, sdst + m * 1024);
+    } else {
+        // base row b0 <= every row copied, so lane offsets stay >= 0
+        const int b0 = max(min(row0, n - TR), 0);
+        const int r = lane >> 4;
+        const int row = min(row0 + 4 * m + r, n - 1);
+        const unsigned o = off + (unsigned)((row - b0 - r) * row_bytes);
+        dma16((const char *)base + b0 * row_bytes, o, sdst + m * 1024);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // dQ: workgroup = 4 waves x 32 query rows of one (batch, head); 32-key tiles
-// of K (R and T layouts) and V (R layout) double-buffered in LDS.
+// of K and V stream through NSQ stages, PDQ tiles ahead.  Each wave copies
+// rows 4w.. and 4(w+4).. of both tiles.
+constexpr int NWB = 4;
+constexpr int NSQ = 4;
+constexpr int PDQ = NSQ - 1;
+constexpr int STAGE_DQ = 2 * TB;           // K, V
+
 __global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[2 * 3 * TB];
+    __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
@@ -140,8 +195,12 @@ attn_bwd_dq(BwdParams p) {
     load_b_rows(p.q + qoff, hi, qf);
     load_b_rows(p.dout + qoff, hi, df);
     const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + p.q_row0 + qr;
-    const float lq = p.lse[lrow] * 1.4426950408889634f;
+    const float lq = p.lse[lrow] * LOG2E;
     const float dq_d = p.delta[lrow];
+    settle(qf);
+    settle(df);
+    settle(lq);
+    settle(dq_d);
     f32x16 acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -150,65 +209,89 @@ attn_bwd_dq(BwdParams p) {
 
     const uint16_t *kb = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
     const uint16_t *vb = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
-    const int64_t ks = (int64_t)p.hkv * D;
-    u32x4 kreg[CPT], vreg[CPT];
-    auto gload = [&](int t) {
+    const int64_t row_bytes = (int64_t)p.hkv * D * 2;
+    const unsigned coff = copy_offset(lane, wave, row_bytes);   // m = wave, wave + 4
+    // tiles past the last repeat it, so every wave issues 4 copies per tile
+    auto issue = [&](int t, int stage) {
+        const int key0 = min(t, ntiles - 1) * TR;
+        const unsigned sb = lbase + stage * STAGE_DQ;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int key = min(t * TR + tile_row(tid, i), p.nk - 1);
-            kreg[i] = *(const u32x4 *)(kb + key * ks + (tid & 15) * 8);
-            vreg[i] = *(const u32x4 *)(vb + key * ks + (tid & 15) * 8);
+        for (int i = 0; i < 2; ++i) {
+            copy_rows(kb, row_bytes, key0, p.nk, wave + 4 * i, coff, sb, lane);
+            copy_rows(vb, row_bytes, key0, p.nk, wave + 4 * i, coff, sb + TB, lane);
         }
     };
-    auto lstore = [&](int buf) {
-        char *base = lds + buf * 3 * TB;
+    if (ntiles > 0) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int r = tile_row(tid, i), c = tid & 15;
-            *(u32x4 *)(base + r_off(r, c)) = kreg[i];           // K, R layout
-            *(u32x4 *)(base + TB + t_off(r, c)) = kreg[i];      // K, T layout
-            *(u32x4 *)(base + 2 * TB + r_off(r, c)) = vreg[i];  // V, R layout
-        }
-    };
-    gload(0);
-    lstore(0);
-    __syncthreads();
+        for (int i = 0; i < PDQ; ++i) issue(i, i);
+        wait_vmcnt<4 * (PDQ - 1)>();
+    }
+    lds_barrier();
+    int stage = 0;
     for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) gload(t + 1);
+        int ns = stage + PDQ;
+        if (ns >= NSQ) ns -= NSQ;
+        issue(t + PDQ, ns);
         if (t < wtiles) {
-            const unsigned sK = lbase + (t & 1) * 3 * TB, sKT = sK + TB, sV = sK + 2 * TB;
+            const unsigned sK = lbase + stage * STAGE_DQ, sV = sK + TB;
+            // the tile's LDS operands are read ahead of the products
+            // (the transposed K^T reads go out behind the S, dP products)
+            bf16x8 ak[D / 16], av[D / 16], at[2][D / 32];
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                ak[kk] = k_read(sK + L.roff(kk));
+                av[kk] = k_read(sV + L.roff(kk));
+            }
+            __builtin_amdgcn_sched_barrier(0);
             f32x16 s = {}, dp = {};
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                s = MFMA(k_read(sK + L.roff[kk]), qf[kk], s, 0, 0, 0);
-                dp = MFMA(k_read(sV + L.roff[kk]), df[kk], dp, 0, 0, 0);
+                s = MFMA(ak[kk], qf[kk], s, 0, 0, 0);
+                dp = MFMA(av[kk], df[kk], dp, 0, 0, 0);
             }
-            const int key0 = t * TR;
-            bf16x8 dsb[2];
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                f32x8 ds;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int key = key0 + 16 * kc + 8 * hi + e;
-                    const bool vis = key < p.nk && (!p.causal || key <= qrow);
-                    const float pr = vis ? __builtin_amdgcn_exp2f(
-                                               __builtin_fmaf(s[kc * 8 + e], p.scale_log2, -lq))
-                                         : 0.0f;
-                    ds[e] = pr * (dp[kc * 8 + e] - dq_d);
-                }
-                dsb[kc] = __builtin_convertvector(ds, bf16x8);
-            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-                    acc[dt] = MFMA(vt_read(sKT + L.toff[dt] + kc * 16 * RB), dsb[kc], acc[dt], 0,
-                                   0, 0);
+                    at[kc][dt] = vt_read2(sK + L.toff(dt, 0) + kc * 16 * RB,
+                                          sK + L.toff(dt, 1) + kc * 16 * RB);
+            __builtin_amdgcn_sched_barrier(0);
+            const int key0 = t * TR;
+            // tile entirely visible to the wave's rows: no mask
+            const bool full = key0 + TR <= p.nk && (!p.causal || key0 + TR - 1 <= wrow0);
+            bf16x8 dsb[2];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                f32x8 x, ds;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(s[kc * 8 + e], p.scale_log2, -lq);
+                if (!full) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int key = key0 + 16 * kc + 8 * hi + e;
+                        const bool vis = key < p.nk && (!p.causal || key <= qrow);
+                        x[e] = vis ? x[e] : -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    ds[e] = __builtin_amdgcn_exp2f(x[e]) * (dp[kc * 8 + e] - dq_d);
+                dsb[kc] = __builtin_convertvector(ds, bf16x8);
+            }
+            // dQ^T += K^T dS^T
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+                    acc[dt] = MFMA(at[kc][dt], dsb[kc], acc[dt], 0, 0, 0);
         }
-        if (t + 1 < ntiles) lstore((t + 1) & 1);
-        __syncthreads();
+        wait_vmcnt<4 * (PDQ - 1)>();   // tile t + 1 has landed
+        lds_barrier();
+        stage = stage + 1 == NSQ ? 0 : stage + 1;
     }
+    wait_vmcnt<0>();
 
     // dq[row] += scale * dQ: lane holds head dims dt*32 + 8*i + 4*hi + j
     if (qrow < p.nq) {
@@ -235,13 +318,18 @@ attn_bwd_dq(BwdParams p) {
 // computed once, and each wave fits in half the register file, so the two
 // waves of a key group share a SIMD and overlap their vector and matrix work.
 // The workgroup streams 32-row tiles of Q and dO (with L and D) for hpw
-// query heads of the group; the group's heads are split over head_splits
-// workgroups, which sum into dk, dv with fp32 atomics.
+// query heads of the group through NSK stages, PDK tiles ahead; the group's
+// heads are split over head_splits workgroups, which sum into dk, dv with
+// fp32 atomics.  Wave w copies rows 4w .. 4w+3 of Q and dO and, into a slot
+// of its own, the tile's L (lanes 0-31) and D (lanes 32-63).
 constexpr int NWK = 8;                         // waves per dK/dV workgroup
 constexpr int KW = 4;                          // key groups of 32 per workgroup
-constexpr int TBUF = 4 * TB + 2 * TR * 4;      // one tile: Q R, Q T, dO R, dO T, L, D
+constexpr int NSK = 5;                         // stages: PDK ahead + the two tiles in use
+constexpr int PDK = NSK - 2;
+constexpr int LD_SLOT = 64 * 4;                // one wave's L and D of a tile
+constexpr int STAGE_DKDV = 2 * TB + NWK * LD_SLOT;   // Q, dO, L/D slots
 constexpr int PSLAB = 64 * 16 * 4;             // one key group's fp32 P of a tile
-constexpr int DKDV_LDS = 3 * TBUF + 2 * KW * PSLAB;
+constexpr int DKDV_LDS = NSK * STAGE_DKDV + 2 * KW * PSLAB;
 
 __global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv(BwdParams p) {
@@ -268,7 +356,6 @@ attn_bwd_dkdv(BwdParams p) {
     LaneOffsets L;
     L.init(lane);
     const unsigned lbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
-    float *pslab0 = (float *)(lds + 3 * TBUF + kwave * PSLAB);
 
     // this lane's key: K (P waves) or V (dS waves) as B operands
     const int key = wkey0 + l32;
@@ -276,6 +363,7 @@ attn_bwd_dkdv(BwdParams p) {
     const int64_t koff = ((n * p.two_c + kr) * (int64_t)p.hkv + g) * D;
     bf16x8 bf[D / 16];
     load_b_rows((ds_wave ? p.v : p.k) + koff, hi, bf);
+    settle(bf);
     f32x16 acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -288,75 +376,86 @@ attn_bwd_dkdv(BwdParams p) {
     const int nqt = (p.nq + TR - 1) / TR;
     const int per_head = max(nqt - qstart, 0);
     const int ntiles = per_head * hpw;
-    u32x4 qreg, dreg;
-    float lreg = 0.0f, dreg1 = 0.0f;
-    auto gload = [&](int u) {
+    const int64_t row_bytes = (int64_t)p.hq * D * 2;
+    const unsigned coff = copy_offset(lane, wave, row_bytes);
+    const int64_t qrow_base = (int64_t)n * p.two_c + p.q_row0;   // global row of local row 0
+    // tiles past the last repeat it, so every wave issues 3 copies per tile
+    auto issue = [&](int u, int stage) {
+        u = min(u, ntiles - 1);
         const int head = h0 + u / per_head;
-        const int qt = qstart + u % per_head;
-        const int row = min(qt * TR + tid / 16, p.nq - 1);
-        const int64_t off = ((n * p.two_c + p.q_row0 + row) * (int64_t)p.hq + head) * D;
-        qreg = *(const u32x4 *)(p.q + off + (tid & 15) * 8);
-        dreg = *(const u32x4 *)(p.dout + off + (tid & 15) * 8);
-        if (tid < TR) {
-            const int lrow_q = min(qt * TR + tid, p.nq - 1);
-            const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + p.q_row0 + lrow_q;
-            lreg = p.lse[lrow] * 1.4426950408889634f;
-            dreg1 = p.delta[lrow];
-        }
-    };
-    auto lstore = [&](int buf) {
-        char *base = lds + buf * TBUF;
-        const int r = tid / 16, c = tid & 15;
-        *(u32x4 *)(base + r_off(r, c)) = qreg;
-        *(u32x4 *)(base + TB + t_off(r, c)) = qreg;
-        *(u32x4 *)(base + 2 * TB + r_off(r, c)) = dreg;
-        *(u32x4 *)(base + 3 * TB + t_off(r, c)) = dreg;
-        if (tid < TR) {
-            ((float *)(base + 4 * TB))[tid] = lreg;
-            ((float *)(base + 4 * TB + TR * 4))[tid] = dreg1;
-        }
+        const int row0 = (qstart + u % per_head) * TR;
+        const unsigned sb = lbase + stage * STAGE_DKDV;
+        const int64_t e0 = qrow_base * p.hq * D + (int64_t)head * D;
+        copy_rows(p.q + e0, row_bytes, row0, p.nq, wave, coff, sb, lane);
+        copy_rows(p.dout + e0, row_bytes, row0, p.nq, wave, coff, sb + TB, lane);
+        const int lr = min(row0 + l32, p.nq - 1);
+        const int64_t li = ((int64_t)n * p.hq + head) * p.two_c + p.q_row0 + lr;
+        dma4((hi ? p.delta : p.lse) + li, sb + 2 * TB + wave * LD_SLOT);
     };
     if (ntiles > 0) {
-        gload(0);
-        lstore(0);
+#pragma unroll
+        for (int i = 0; i < PDK; ++i) issue(i, i);
+        wait_vmcnt<3 * (PDK - 1)>();
     }
-    __syncthreads();
-    // iteration it: P waves on tile it, dS waves on tile it - 1; tile u sits
-    // in buffer u % 3 and its P in slab u % 2
-    int buf_p = 0, buf_ds = 2, buf_next = 1;
+    lds_barrier();
+    // Iteration it: P waves on tile it (S, P, dV), dS waves one tile behind
+    // (dP, dS, dK); every LDS operand of a tile is read ahead of its products.
+    const unsigned slab0 = lbase + NSK * STAGE_DKDV + kwave * PSLAB;
+    int st_p = 0, st_ds = NSK - 1;
     for (int it = 0; ntiles > 0 && it <= ntiles; ++it) {
-        if (it + 1 < ntiles) gload(it + 1);
+        int ns = st_p + PDK;
+        if (ns >= NSK) ns -= NSK;
+        issue(it + PDK, ns);
         const int u = ds_wave ? it - 1 : it;
         const int q0 = (qstart + (u < 0 ? 0 : u) % per_head) * TR;
-        // the tile exists and some row of it sees the wave's keys
         if (u >= 0 && u < ntiles && (!p.causal || q0 + TR - 1 >= wkey0)) {
-            const int buf = ds_wave ? buf_ds : buf_p;
-            const unsigned sT = lbase + buf * TBUF;
-            const char *lb = lds + buf * TBUF + 4 * TB;
-            float *slab = pslab0 + (u & 1) * (KW * PSLAB / 4);
+            const unsigned sT = lbase + (ds_wave ? st_ds : st_p) * STAGE_DKDV;
+            const unsigned lslot = sT + 2 * TB + wave * LD_SLOT;
+            const unsigned slab = slab0 + (u & 1) * (KW * PSLAB);
+            const unsigned sR = ds_wave ? sT + TB : sT;
+            const unsigned sA = ds_wave ? sT : sT + TB;
+            bf16x8 ar[D / 16], at[2][D / 32];
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(sR + L.roff(kk));
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+                    at[qc][dt] = vt_read2(sA + L.toff(dt, 0) + qc * 16 * RB,
+                                          sA + L.toff(dt, 1) + qc * 16 * RB);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 s = {};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) s = MFMA(ar[kk], bf[kk], s, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
             bf16x8 ob[2];
             if (!ds_wave) {
-                f32x16 s = {};
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk)
-                    s = MFMA(k_read(sT + L.roff[kk]), bf[kk], s, 0, 0, 0);
-                f32x16 pv;
+                const bool full = q0 + TR <= p.nq && wkey0 + TR <= p.nk &&
+                                  (!p.causal || wkey0 + TR - 1 <= q0);
+                f32x16 x;
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc) {
-                    const f32x8 lv = *(const f32x8 *)(lb + (16 * qc + 8 * hi) * 4);
+                    const f32x8 lv = *(const __attribute__((address_space(3))) f32x8 *)(
+                        uintptr_t)(lslot + (16 * qc + 8 * hi) * 4);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int row = q0 + 16 * qc + 8 * hi + e;
+                    for (int e = 0; e < 8; ++e)
+                        x[qc * 8 + e] = __builtin_fmaf(s[qc * 8 + e], p.scale_log2, -LOG2E * lv[e]);
+                }
+                if (!full) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int row = q0 + 16 * (i >> 3) + 8 * hi + (i & 7);
                         const bool vis = row < p.nq && key < p.nk && (!p.causal || key <= row);
-                        pv[qc * 8 + e] =
-                            vis ? __builtin_amdgcn_exp2f(
-                                      __builtin_fmaf(s[qc * 8 + e], p.scale_log2, -lv[e]))
-                                : 0.0f;
+                        x[i] = vis ? x[i] : -INFINITY;
                     }
                 }
+                f32x16 pv;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(x[i]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    *(f32x4 *)(slab + (j * 64 + lane) * 4) =
+                    *(__attribute__((address_space(3))) f32x4 *)(uintptr_t)(
+                        slab + (j * 64 + lane) * 16) =
                         f32x4{pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]};
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc) {
@@ -366,39 +465,36 @@ attn_bwd_dkdv(BwdParams p) {
                     ob[qc] = __builtin_convertvector(h, bf16x8);
                 }
             } else {
-                f32x16 dp = {};
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk)
-                    dp = MFMA(k_read(sT + 2 * TB + L.roff[kk]), bf[kk], dp, 0, 0, 0);
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc) {
-                    const f32x8 dv8 = *(const f32x8 *)(lb + TR * 4 + (16 * qc + 8 * hi) * 4);
-                    const f32x4 pa = *(const f32x4 *)(slab + ((2 * qc) * 64 + lane) * 4);
-                    const f32x4 pb = *(const f32x4 *)(slab + ((2 * qc + 1) * 64 + lane) * 4);
+                    const f32x8 dv8 = *(const __attribute__((address_space(3))) f32x8 *)(
+                        uintptr_t)(lslot + TR * 4 + (16 * qc + 8 * hi) * 4);
+                    const f32x4 pa = *(const __attribute__((address_space(3))) f32x4 *)(
+                        uintptr_t)(slab + ((2 * qc) * 64 + lane) * 16);
+                    const f32x4 pb = *(const __attribute__((address_space(3))) f32x4 *)(
+                        uintptr_t)(slab + ((2 * qc + 1) * 64 + lane) * 16);
                     f32x8 ds;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        ds[e] = pa[e] * (dp[qc * 8 + e] - dv8[e]);
-                        ds[4 + e] = pb[e] * (dp[qc * 8 + 4 + e] - dv8[4 + e]);
+                        ds[e] = pa[e] * (s[qc * 8 + e] - dv8[e]);
+                        ds[4 + e] = pb[e] * (s[qc * 8 + 4 + e] - dv8[4 + e]);
                     }
                     ob[qc] = __builtin_convertvector(ds, bf16x8);
                 }
             }
-            // P waves: dV^T += dO^T P;  dS waves: dK^T += Q^T dS
-            const unsigned sA = sT + (ds_wave ? TB : 3 * TB);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc)
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-                    acc[dt] = MFMA(vt_read(sA + L.toff[dt] + qc * 16 * RB), ob[qc], acc[dt], 0,
-                                   0, 0);
+                    acc[dt] = MFMA(at[qc][dt], ob[qc], acc[dt], 0, 0, 0);
         }
-        if (it + 1 < ntiles) lstore(buf_next);
-        __syncthreads();
-        buf_ds = buf_p;
-        buf_p = buf_next;
-        buf_next = buf_next == 2 ? 0 : buf_next + 1;
+        wait_vmcnt<3 * (PDK - 1)>();   // tile it + 1 has landed
+        lds_barrier();
+        st_ds = st_p;
+        st_p = st_p + 1 == NSK ? 0 : st_p + 1;
     }
+    wait_vmcnt<0>();
 
     // dv += dV (P waves), dk += scale dK (dS waves); lane holds head dims
     // dt*32 + 8*i + 4*hi + j.  Split heads add with atomics.

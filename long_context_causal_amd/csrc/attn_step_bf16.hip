@@ -185,25 +185,6 @@ struct FusedPlan {
     }
 };
 
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// One direct global -> LDS copy of 16 bytes per lane from base + off (base
-// wave-uniform, in SGPRs; off a per-lane byte offset); lane L writes
-// lds_base + 16*L.  m0 carries the LDS base; one wait state separates its
-// write from the copy that reads it.
-__device__ __forceinline__ void dma16(const void *base, unsigned off, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off), "s"(base), "s"(lds_base)
-                 : "memory");
-}
-
 template <class Plan, bool OUT_BF16>
 struct Kernel {
     // Per-wave state.

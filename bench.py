@@ -45,21 +45,28 @@ def parse():
     return ap.parse_args()
 
 
+# the sources the forward attention kernels are built from (their digest
+# ties a committed counter summary to the code it was measured on)
+KERNEL_SOURCES = ("attn_step_bf16.hip", "mfma_tiles.h")
+
+
 def committed_traffic(workload, key="attention_traffic_bytes_per_launch"):
     """HBM bytes per launch of the attention kernel (key: the step kernel's
     or the fused kernel's line) from the committed counter summary.
 
-    The summary records the sha256 of the kernel source it was measured
-    with; if the source has changed since, the figure no longer describes
-    this kernel and None is returned.
+    The summary records the sha256 of the kernel sources it was measured
+    with (KERNEL_SOURCES, concatenated); if they have changed since, the
+    figure no longer describes this kernel and None is returned.
     """
     import hashlib
-    src = os.path.join(ROOT, "long_context_causal_amd", "csrc", "attn_step_bf16.hip")
     prof = os.path.join(ROOT, "profiles", f"attn_step_bf16__{workload}__hbm_traffic.txt")
     if not os.path.exists(prof):
         return None
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_causal_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    digest = h.hexdigest()
     recorded, traffic = None, None
     with open(prof) as f:
         for line in f:

@@ -17,7 +17,11 @@ method, in the pages' order:
   ring source of each step, blockwise step attention, the per-step L
   correction and the final O merge, RoPE at global positions, and the
   backward of each ring step with the rank's final L (the K/V gradient
-  contributions a reduce-scatter would sum on their owner).
+  contributions a reduce-scatter would sum on their owner);
+* ``varlen``     - packed variable-length samples: each sample an
+  independent causal sequence, split by the zigzag rule on its own, RoPE at
+  in-sample positions (reset at every sample start), and the rank's CP
+  share of the packed batch.
 
 Pins (tests marked ``not gpu``) tie both to things other than themselves:
 closed forms, a library attention routine, exact integer cover of the
@@ -29,3 +33,4 @@ rotate-half pairing), which the pages do not fix.
 from .attention import (attention_rows, attention_rows_bwd, causal_attention,  # noqa: F401
                         causal_attention_bwd, max_threads)
 from . import cp  # noqa: F401
+from . import varlen  # noqa: F401

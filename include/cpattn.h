@@ -96,6 +96,25 @@ typedef struct cpattn_partial {
     int64_t rows;        /* number of local rows it covers                   */
 } cpattn_partial;
 
+/* Packed variable-length samples ("Megatron 面试题（一）", M016 follow-up:
+ * positions are reset at each packed sample's boundary).  Every batch
+ * element packs the same nseq samples along its sequence axis: sample i is
+ * rows [cu_seqlens[i], cu_seqlens[i+1]) of the s rows, an independent
+ * causal sequence (no row sees another sample) whose positions restart at
+ * 0.  Each sample is split by the zigzag rule on its own: rank r holds its
+ * chunk r, then its chunk 2cp-1-r, samples in packing order, so sample i
+ * occupies local rows [cu_seqlens[i]/cp, cu_seqlens[i+1]/cp) of every rank.
+ * cu_seqlens: caller-owned HOST array of nseq + 1 offsets, cu_seqlens[0] =
+ * 0, cu_seqlens[nseq] = s, every sample length a positive multiple of 2*cp
+ * (ESHAPE otherwise); 1 <= nseq <= CPATTN_MAX_SEQS.  Read during the call
+ * only. */
+typedef struct cpattn_varlen {
+    int32_t nseq;
+    const int64_t *cu_seqlens;
+} cpattn_varlen;
+
+#define CPATTN_MAX_SEQS 128
+
 #define CPATTN_MAX_PARTIALS 64
 #define CPATTN_MAX_MERGE_WEIGHTS 8192   /* hq * n per merge call */
 
@@ -225,6 +244,37 @@ int cpattn_backward(const cpattn_dims *dims, int dtype, float scale, int rank,
                     const void *qz, const void *kz, const void *vz, const float *o_r,
                     const void *do_r, const float *lse_r, float *delta_ws, float *dq_r,
                     float *dkz, float *dvz, void *stream);
+
+/* Packed variable-length forms of the partition and of the fused forward
+ * (see cpattn_varlen for the layout).  vl = NULL, or nseq = 1, gives the
+ * unpacked call.
+ *
+ * cpattn_partition_positions_varlen, host, pure: the in-sample positions
+ * of rank 'rank''s s/cp local rows into pos (caller-owned host array of
+ * s/cp int32).  EINVAL for a NULL pos or offset array or a rank out of
+ * range, ESHAPE for bad offsets or cp > CPATTN_MAX_PARTIALS. */
+int cpattn_partition_positions_varlen(int64_t s, int cp, int rank, const cpattn_varlen *vl,
+                                      int32_t *pos);
+
+/* cpattn_partition_varlen, device: x [b, s, h, d] -> xz [cp, b, s/cp, h, d],
+ * each sample split on its own; pos_dev (optional) [cp, s/cp] receives the
+ * in-sample positions; rope (optional) rotates each row at its in-sample
+ * position.  Otherwise as cpattn_partition. */
+int cpattn_partition_varlen(const cpattn_dims *dims, int dtype, int h, const cpattn_varlen *vl,
+                            const void *x, void *xz, int32_t *pos_dev,
+                            const cpattn_rope *rope, void *stream);
+
+/* cpattn_forward_fused_varlen, device: rank 'rank''s whole forward share of
+ * a packed batch in one launch.  Each sample's rows stream the key blocks
+ * of the cp ring steps of that sample only (cpattn_forward_fused on every
+ * sample at once).  qz, kz, vz [cp, b, s/cp, h, 128] bf16 as written by
+ * cpattn_partition_varlen; o_out [b, s/cp, hq, 128] (out_dtype); lse_out
+ * [b, hq, s/cp] or NULL.  Types, alignment and errors as
+ * cpattn_forward_fused. */
+int cpattn_forward_fused_varlen(const cpattn_dims *dims, int dtype, float scale, int rank,
+                                const cpattn_varlen *vl, const void *qz, const void *kz,
+                                const void *vz, int out_dtype, void *o_out, float *lse_out,
+                                void *stream);
 
 /* Static name of a status code. */
 const char *cpattn_status_str(int status);

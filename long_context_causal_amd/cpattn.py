@@ -23,6 +23,7 @@ CPATTN_Q_SECOND_HALF = 2
 CPATTN_OK, CPATTN_EINVAL, CPATTN_ESHAPE, CPATTN_EDTYPE, CPATTN_EALIGN, \
     CPATTN_ENOSPACE, CPATTN_EHIP = range(7)
 CPATTN_MAX_PARTIALS = 64
+CPATTN_MAX_SEQS = 128
 
 
 class cpattn_dims(ctypes.Structure):
@@ -37,6 +38,18 @@ class cpattn_rope(ctypes.Structure):
 class cpattn_partial(ctypes.Structure):
     _fields_ = [("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("row0", ctypes.c_int64), ("rows", ctypes.c_int64)]
+
+
+class cpattn_varlen(ctypes.Structure):
+    _fields_ = [("nseq", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int64))]
+
+
+def make_varlen(cu_seqlens):
+    """A cpattn_varlen over a host copy of the offsets; keep the returned
+    pair alive for the call (the struct points into the array)."""
+    arr = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    vl = cpattn_varlen(arr.size - 1, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    return vl, arr
 
 
 class CpattnError(RuntimeError):
@@ -71,6 +84,12 @@ def lib():
         L.cpattn_forward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, ctypes.c_size_t,
                                      I, P, P, P]
         L.cpattn_forward_fused.argtypes = [D, I, ctypes.c_float, I, P, P, P, I, P, P, P]
+        V = ctypes.POINTER(cpattn_varlen)
+        L.cpattn_partition_positions_varlen.argtypes = [ctypes.c_int64, I, I, V,
+                                                        ctypes.POINTER(ctypes.c_int32)]
+        L.cpattn_partition_varlen.argtypes = [D, I, I, V, P, P, P, ctypes.POINTER(cpattn_rope), P]
+        L.cpattn_forward_fused_varlen.argtypes = [D, I, ctypes.c_float, I, V, P, P, P, I, P, P,
+                                                  P]
         L.cpattn_bwd_delta.argtypes = [D, P, P, P, P]
         L.cpattn_step_bwd.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P]
         L.cpattn_backward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P, P]
@@ -79,7 +98,8 @@ def lib():
         for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
                      "cpattn_step_fwd", "cpattn_merge", "cpattn_forward",
                      "cpattn_forward_fused", "cpattn_bwd_delta", "cpattn_step_bwd",
-                     "cpattn_backward"):
+                     "cpattn_backward", "cpattn_partition_positions_varlen",
+                     "cpattn_partition_varlen", "cpattn_forward_fused_varlen"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -192,3 +212,36 @@ def cpattn_backward(dims, dtype, scale, rank, qz, kz, vz, o_r, do_r, lse_r, delt
                                  _ptr(kz), _ptr(vz), _ptr(o_r), _ptr(do_r), _ptr(lse_r),
                                  _ptr(delta_ws), _ptr(dq_r), _ptr(dkz), _ptr(dvz),
                                  _stream(stream)), "cpattn_backward")
+
+
+def cpattn_partition_positions_varlen(s, cp, rank, cu_seqlens):
+    if s % cp != 0:
+        raise CpattnError(CPATTN_ESHAPE, "cpattn_partition_positions_varlen")
+    vl, keep = make_varlen(cu_seqlens)
+    out = np.empty(s // cp, dtype=np.int32)
+    _check(lib().cpattn_partition_positions_varlen(
+        s, cp, rank, ctypes.byref(vl), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+        "cpattn_partition_positions_varlen")
+    del keep
+    return out
+
+
+def cpattn_partition_varlen(dims, dtype, h, cu_seqlens, x, xz, pos=None, rope_theta=None,
+                            stream=None):
+    vl, keep = make_varlen(cu_seqlens)
+    rope = ctypes.byref(cpattn_rope(rope_theta)) if rope_theta is not None else None
+    _check(lib().cpattn_partition_varlen(ctypes.byref(dims), dtype, h, ctypes.byref(vl),
+                                         _ptr(x), _ptr(xz), _ptr(pos), rope, _stream(stream)),
+           "cpattn_partition_varlen")
+    del keep
+
+
+def cpattn_forward_fused_varlen(dims, dtype, scale, rank, cu_seqlens, qz, kz, vz, out_dtype,
+                                o_out, lse_out=None, stream=None):
+    vl, keep = make_varlen(cu_seqlens)
+    _check(lib().cpattn_forward_fused_varlen(ctypes.byref(dims), dtype, float(scale), rank,
+                                             ctypes.byref(vl), _ptr(qz), _ptr(kz), _ptr(vz),
+                                             out_dtype, _ptr(o_out), _ptr(lse_out),
+                                             _stream(stream)),
+           "cpattn_forward_fused_varlen")
+    del keep

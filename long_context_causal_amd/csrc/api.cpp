@@ -54,6 +54,29 @@ int check_dims(const cpattn_dims *dims) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? CPATTN_OK : CPATTN_EHIP; }
 
+// The packed samples of a batch element as kernel arguments (vl == NULL: one
+// sample of s rows).  ESHAPE unless the offsets run from 0 to s in positive
+// steps that are multiples of 2cp; EINVAL for a NULL offset array.
+int make_table(int64_t s, int cp, const cpattn_varlen *vl, cpattn::SeqTable &t) {
+    memset(&t, 0, sizeof(t));
+    if (vl == nullptr) {
+        t.nseq = 1;
+        t.lcu[1] = (int32_t)(s / cp);
+        return CPATTN_OK;
+    }
+    if (vl->cu_seqlens == nullptr) return CPATTN_EINVAL;
+    if (vl->nseq < 1 || vl->nseq > CPATTN_MAX_SEQS) return CPATTN_ESHAPE;
+    const int64_t *cu = vl->cu_seqlens;
+    if (cu[0] != 0 || cu[vl->nseq] != s) return CPATTN_ESHAPE;
+    t.nseq = vl->nseq;
+    for (int i = 0; i < vl->nseq; ++i) {
+        const int64_t len = cu[i + 1] - cu[i];
+        if (len <= 0 || len % (2 * (int64_t)cp) != 0) return CPATTN_ESHAPE;
+        t.lcu[i + 1] = (int32_t)(cu[i + 1] / cp);
+    }
+    return CPATTN_OK;
+}
+
 int64_t step_rows(const cpattn_dims &d, int mode) {
     const int64_t c = d.s / (2 * d.cp);
     return mode == CPATTN_Q_SECOND_HALF ? c : 2 * c;
@@ -109,8 +132,9 @@ int cpattn_partition_positions(int64_t s, int cp, int rank, int32_t *pos) {
     return CPATTN_OK;
 }
 
-int cpattn_partition(const cpattn_dims *dims, int dtype, int h, const void *x, void *xz,
-                     int32_t *pos_dev, const cpattn_rope *rope, void *stream) {
+int cpattn_partition_varlen(const cpattn_dims *dims, int dtype, int h, const cpattn_varlen *vl,
+                            const void *x, void *xz, int32_t *pos_dev, const cpattn_rope *rope,
+                            void *stream) {
     int st = check_dims(dims);
     if (st) return st;
     if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return CPATTN_EDTYPE;
@@ -120,8 +144,33 @@ int cpattn_partition(const cpattn_dims *dims, int dtype, int h, const void *x, v
         return CPATTN_EALIGN;
     if (rope != nullptr && !(rope->theta > 0.0)) return CPATTN_EINVAL;
     if (dims->s > INT32_MAX) return CPATTN_ESHAPE;
-    return status_of(cpattn::launch_partition(*dims, dtype, h, x, xz, pos_dev, rope,
+    cpattn::SeqTable t;
+    st = make_table(dims->s, dims->cp, vl, t);
+    if (st) return st;
+    return status_of(cpattn::launch_partition(*dims, dtype, h, t, x, xz, pos_dev, rope,
                                               (hipStream_t)stream));
+}
+
+int cpattn_partition(const cpattn_dims *dims, int dtype, int h, const void *x, void *xz,
+                     int32_t *pos_dev, const cpattn_rope *rope, void *stream) {
+    return cpattn_partition_varlen(dims, dtype, h, nullptr, x, xz, pos_dev, rope, stream);
+}
+
+int cpattn_partition_positions_varlen(int64_t s, int cp, int rank, const cpattn_varlen *vl,
+                                      int32_t *pos) {
+    if (pos == nullptr || cp < 1 || rank < 0 || rank >= cp) return CPATTN_EINVAL;
+    if (cp > CPATTN_MAX_PARTIALS) return CPATTN_ESHAPE;
+    if (s < 1 || s % (2 * (int64_t)cp) != 0 || s > INT32_MAX) return CPATTN_ESHAPE;
+    cpattn::SeqTable t;
+    const int st = make_table(s, cp, vl, t);
+    if (st) return st;
+    for (int i = 0; i < t.nseq; ++i) {
+        const int64_t l0 = t.lcu[i], c = (t.lcu[i + 1] - l0) / 2;
+        const int64_t big = 2 * (int64_t)cp - 1 - rank;
+        for (int64_t j = 0; j < c; ++j) pos[l0 + j] = (int32_t)(rank * c + j);
+        for (int64_t j = 0; j < c; ++j) pos[l0 + c + j] = (int32_t)(big * c + j);
+    }
+    return CPATTN_OK;
 }
 
 int cpattn_step_fwd(const cpattn_dims *dims, int dtype, float scale, int mode,
@@ -235,11 +284,18 @@ int cpattn_forward(const cpattn_dims *dims, int dtype, float scale, int rank, co
     return cpattn_merge(dims, dims->cp, parts, out_dtype, o_out, lse_out, stream);
 }
 
-int cpattn_forward_fused(const cpattn_dims *dims, int dtype, float scale, int rank,
-                         const void *qz, const void *kz, const void *vz, int out_dtype,
-                         void *o_out, float *lse_out, void *stream) {
+int cpattn_forward_fused_varlen(const cpattn_dims *dims, int dtype, float scale, int rank,
+                                const cpattn_varlen *vl, const void *qz, const void *kz,
+                                const void *vz, int out_dtype, void *o_out, float *lse_out,
+                                void *stream) {
     int st = check_dims(dims);
     if (st) return st;
+    cpattn::SeqTable t;
+    st = make_table(dims->s, dims->cp, vl, t);
+    if (st) return st;
+    // query tiles of 256 rows, sample by sample (the grid is 32-bit)
+    if (((dims->s / dims->cp) / 256 + t.nseq) * dims->hq * dims->b > (int64_t)INT32_MAX)
+        return CPATTN_ESHAPE;
     if (rank < 0 || rank >= dims->cp) return CPATTN_EINVAL;
     if (!qz || !kz || !vz || !o_out) return CPATTN_EINVAL;
     if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
@@ -257,10 +313,18 @@ int cpattn_forward_fused(const cpattn_dims *dims, int dtype, float scale, int ra
     f.rank = rank;
     f.cp = dims->cp;
     f.scale_log2 = g.scale_log2;
+    f.tab = t;
     const hipError_t e = cpattn::launch_fused_bf16(f, qz, kz, vz, o_out,
                                                    out_dtype == CPATTN_BF16, lse_out,
                                                    (hipStream_t)stream);
     return e == hipSuccess ? CPATTN_OK : CPATTN_EHIP;
+}
+
+int cpattn_forward_fused(const cpattn_dims *dims, int dtype, float scale, int rank,
+                         const void *qz, const void *kz, const void *vz, int out_dtype,
+                         void *o_out, float *lse_out, void *stream) {
+    return cpattn_forward_fused_varlen(dims, dtype, scale, rank, nullptr, qz, kz, vz, out_dtype,
+                                       o_out, lse_out, stream);
 }
 
 int cpattn_bwd_delta(const cpattn_dims *dims, const float *o_r, const void *do_r,

@@ -93,10 +93,11 @@ struct Params {
     int64_t two_c, q_row0;
     int nq, nk, hq, hkv, group, num_qtiles;
     float scale_log2;
-    // fused form: the rank, the ring size and the element stride between
-    // the partitioned blocks of consecutive ranks
+    // fused form: the rank, the ring size, the element stride between the
+    // partitioned blocks of consecutive ranks, and the packed samples
     int rank, cp;
     int64_t block_elems;
+    SeqTable tab;
 };
 
 // One tile of the key sequence a workgroup streams: the block it comes from
@@ -111,12 +112,22 @@ struct TileRef {
 };
 
 // One CP step: the source rank's block, the mode's keys.
+// Every plan also names the workgroup's query tile: qtile (its index in its
+// sequence), qrow0 and nq (the local row of the sequence's query row 0 and
+// its query rows), orow0 and orows (the output row of query row 0 and the
+// output rows per batch element).
 template <bool CAUSAL>
 struct StepPlan {
     static constexpr bool kLongestFirst = CAUSAL;   // later causal tiles see more keys
     const uint16_t *kb, *vb;
     int nk, ntiles;
-    __device__ __forceinline__ void init(const Params &p, int qtile, int n, int g) {
+    int qtile, qrow0, nq, orow0, orows;
+    __device__ __forceinline__ void init(const Params &p, int qt, int n, int g) {
+        qtile = qt;
+        qrow0 = (int)p.q_row0;
+        nq = p.nq;
+        orow0 = 0;
+        orows = p.nq;
         kb = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
         vb = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
         nk = p.nk;
@@ -135,7 +146,9 @@ struct StepPlan {
     }
 };
 
-// A rank's whole share.  Segments in streaming order: ranks r-1 .. 0, keys
+// A rank's whole share of one sequence (one packed sample: c is its chunk
+// length, and its rows start at local row lcu of every rank's block).
+// Segments in streaming order: ranks r-1 .. 0, keys
 // [0, c) (steps 1 .. r, kv_first_half); ranks cp-1 .. r+1, keys [0, 2c)
 // (steps r+1 .. cp-1, q_second_half: only rows c .. 2c-1 see them, and the
 // segments are streamed only when some row of the workgroup is one of
@@ -146,13 +159,21 @@ struct FusedPlan {
     const uint16_t *k0, *v0;      // rank 0's block, this batch and KV head
     int64_t block;                // elements between consecutive ranks' blocks
     int r, cp, c, cA, nAB, cB, ta, tb, kend, ntiles, q0;
-    __device__ __forceinline__ void init(const Params &p, int qtile, int n, int g) {
-        k0 = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
-        v0 = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
+    int qtile, qrow0, nq, orow0, orows;
+    __device__ __forceinline__ void init(const Params &p, int qt, int n, int g) {
+        const int i = seq_of(p.tab.tile0, p.tab.nseq, qt);
+        const int l0 = p.tab.lcu[i];
+        qtile = qt - p.tab.tile0[i];
+        c = (p.tab.lcu[i + 1] - l0) >> 1;
+        qrow0 = l0;
+        nq = 2 * c;
+        orow0 = l0;
+        orows = (int)p.two_c;
+        k0 = p.k + (((int64_t)n * p.two_c + l0) * p.hkv + g) * D;
+        v0 = p.v + (((int64_t)n * p.two_c + l0) * p.hkv + g) * D;
         block = p.block_elems;
         r = p.rank;
         cp = p.cp;
-        c = (int)(p.two_c >> 1);
         q0 = qtile * BM;
         cA = (c + BN - 1) / BN;
         cB = (2 * c + BN - 1) / BN;
@@ -378,11 +399,9 @@ struct Kernel {
         const int g = item % p.hkv;
         const int n = item / p.hkv;
         const int head = g * p.group + hh;
-        const int qtile = Plan::kLongestFirst ? p.num_qtiles - 1 - qt_rank : qt_rank;
-        const int wrow0 = qtile * BM + wave * 32;   // first step row of this wave
-
         Plan P;
-        P.init(p, qtile, n, g);
+        P.init(p, Plan::kLongestFirst ? p.num_qtiles - 1 - qt_rank : qt_rank, n, g);
+        const int wrow0 = P.qtile * BM + wave * 32;   // first row of this wave in its sequence
         const int ntiles = P.ntiles;
         State S;
         S.kstride = (int64_t)p.hkv * D;
@@ -432,9 +451,9 @@ struct Kernel {
         issue(S, lds_addr, P.tile(0), wave);
         issue(S, lds_addr + 2 * TILEB, P.tile(1), wave);
         {
-            const int row = min(wrow0 + l32, p.nq - 1);
+            const int row = min(wrow0 + l32, P.nq - 1);
             const uint16_t *src =
-                p.q + ((n * p.two_c + p.q_row0 + row) * (int64_t)p.hq + head) * D + hi * 8;
+                p.q + ((n * p.two_c + P.qrow0 + row) * (int64_t)p.hq + head) * D + hi * 8;
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk)
                 S.qf[kk] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(src + kk * 16));
@@ -478,9 +497,10 @@ struct Kernel {
         // L (natural log).
         const float lt = S.l_run + __shfl_xor(S.l_run, 32);
         const int row = wrow0 + l32;
-        if (row < p.nq) {
+        if (row < P.nq) {
             const float inv = 1.0f / lt;
-            const int64_t base = ((n * (int64_t)p.nq + row) * p.hq + head) * D + 4 * hi;
+            const int64_t orow = (int64_t)n * P.orows + P.orow0 + row;
+            const int64_t base = (orow * p.hq + head) * D + 4 * hi;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -497,7 +517,7 @@ struct Kernel {
                     }
                 }
             if (hi == 0 && p.lse != nullptr)
-                p.lse[((int64_t)n * p.hq + head) * p.nq + row] =
+                p.lse[((int64_t)n * p.hq + head) * P.orows + P.orow0 + row] =
                     (S.m_run + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
         }
     }
@@ -565,11 +585,16 @@ hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
     p.hq = f.hq;
     p.hkv = f.hkv;
     p.group = f.hq / f.hkv;
-    p.num_qtiles = (int)((f.two_c + BM - 1) / BM);
     p.scale_log2 = f.scale_log2;
     p.rank = f.rank;
     p.cp = f.cp;
     p.block_elems = f.b * f.two_c * f.hkv * D;
+    // query tiles sample by sample
+    p.tab = f.tab;
+    p.tab.tile0[0] = 0;
+    for (int i = 0; i < p.tab.nseq; ++i)
+        p.tab.tile0[i + 1] = p.tab.tile0[i] + (p.tab.lcu[i + 1] - p.tab.lcu[i] + BM - 1) / BM;
+    p.num_qtiles = p.tab.tile0[p.tab.nseq];
     if (out_bf16) return launch_kernel(attn_fused_bf16<true>, p, f.b, f.hq, stream);
     return launch_kernel(attn_fused_bf16<false>, p, f.b, f.hq, stream);
 }

@@ -25,7 +25,27 @@ struct StepGeom {
 
 StepGeom step_geom(const cpattn_dims &dims, int mode, float scale);
 
-hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h,
+// The samples packed in each batch element, as kernel arguments: sample i
+// occupies local rows [lcu[i], lcu[i+1]) of every rank (lcu = cu_seqlens /
+// cp); tile0[i] is the first query tile of sample i in a fused launch (set
+// by that launcher).  An unpacked batch is one sample of s rows.
+struct SeqTable {
+    int32_t nseq;
+    int32_t lcu[CPATTN_MAX_SEQS + 1];
+    int32_t tile0[CPATTN_MAX_SEQS + 1];
+};
+
+// Largest i in [0, n) with a[i] <= x (a ascending, a[0] <= x).
+__host__ __device__ inline int seq_of(const int32_t *a, int n, int x) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const SeqTable &tab,
                             const void *x, void *xz, int32_t *pos,
                             const cpattn_rope *rope, hipStream_t stream);
 
@@ -33,16 +53,18 @@ hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k,
                             const void *v, float *o, float *lse,
                             hipStream_t stream);
 
-// Geometry of one rank's fused share (cpattn_forward_fused).
+// Geometry of one rank's fused share (cpattn_forward_fused[_varlen]).
 struct FusedGeom {
     int64_t b;
-    int64_t two_c;
+    int64_t two_c;      // local rows per batch element (s / cp)
     int32_t hq, hkv, rank, cp;
     float scale_log2;
+    SeqTable tab;       // the packed samples (tile0 filled by the launcher)
 };
 
-// qz, kz, vz: the partitioned tensors of all ranks [cp, b, 2c, h, 128] bf16.
-// o: [b, 2c, hq, 128] fp32, or bf16 when out_bf16; lse: [b, hq, 2c] or null.
+// qz, kz, vz: the partitioned tensors of all ranks [cp, b, s/cp, h, 128]
+// bf16.  o: [b, s/cp, hq, 128] fp32, or bf16 when out_bf16; lse:
+// [b, hq, s/cp] or null.
 hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
                              const void *vz, void *o, bool out_bf16, float *lse,
                              hipStream_t stream);

@@ -11,6 +11,12 @@
 // RoPE ("Megatron 面试题（一）", M016): every copied row is rotated at its
 // global position pos_r(j), never at its local index.
 //
+// Packed samples (same page, M016's follow-up: positions reset at packed
+// sample boundaries): each sample is split by the rule above on its own,
+// with c its own chunk length, and occupies local rows [cu/cp, cu'/cp) of
+// every rank; pos_r(j) is then the position within the sample.  An
+// unpacked batch is the one-sample case.
+//
 // Without RoPE the kernel is a pure HBM copy: each workgroup moves a run of
 // whole output rows with 16-byte loads and stores, consecutive lanes on
 // consecutive addresses.  With RoPE each workgroup first builds the row's
@@ -30,51 +36,74 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int NT = 256;
 
+constexpr int MAX_ROWS_PER_BLOCK = 512;   // copy kernel: rows handled per workgroup
+
 struct CopyParams {
     const char *x;
     char *xz;
     int32_t *pos;
-    int64_t s, c, b, rows_total;   // rows_total = cp * b * 2c
+    int64_t s, tloc, b, rows_total;   // tloc = s / cp local rows; rows_total = cp * b * tloc
     int cp;
-    int vecs_per_row;              // 16-byte vectors per row (h*d*es/16)
+    int vecs_per_row;                 // 16-byte vectors per row (h*d*es/16)
     int rows_per_block;
+    SeqTable tab;
 };
 
-__device__ __forceinline__ int64_t global_pos(int64_t r, int64_t j, int64_t c, int cp) {
-    return j < c ? r * c + j : (2 * cp - 1 - r) * c + (j - c);
+// Local row j of rank r -> its row in the batch element's packed sequence
+// (src) and its position within its sample (pos).
+__device__ __forceinline__ void source_row(const SeqTable &t, int cp, int64_t r, int64_t j,
+                                           int64_t &src, int64_t &pos) {
+    const int i = seq_of(t.lcu, t.nseq, (int)j);
+    const int64_t c = (t.lcu[i + 1] - t.lcu[i]) / 2;
+    const int64_t jj = j - t.lcu[i];
+    pos = jj < c ? r * c + jj : (2 * cp - 1 - r) * c + (jj - c);
+    src = (int64_t)t.lcu[i] * cp + pos;
 }
 
 // Output row index -> (rank, batch, local row)
-__device__ __forceinline__ void split_row(int64_t row, int64_t b, int64_t two_c,
+__device__ __forceinline__ void split_row(int64_t row, int64_t b, int64_t tloc,
                                           int64_t &r, int64_t &n, int64_t &j) {
-    j = row % two_c;
-    int64_t rn = row / two_c;
+    j = row % tloc;
+    int64_t rn = row / tloc;
     n = rn % b;
     r = rn / b;
 }
 
+// positions of every rank: pos[r * tloc + j]
+__device__ __forceinline__ void write_positions(const SeqTable &t, int cp, int64_t tloc,
+                                                int32_t *pos) {
+    const int64_t total = (int64_t)cp * tloc;
+    for (int64_t i = threadIdx.x; i < total; i += NT) {
+        int64_t src, ps;
+        source_row(t, cp, i / tloc, i % tloc, src, ps);
+        pos[i] = (int32_t)ps;
+    }
+}
+
 __global__ void __launch_bounds__(NT) partition_copy(CopyParams p) {
+    __shared__ int64_t srow[MAX_ROWS_PER_BLOCK];   // source row of each row of the block
     const int64_t row0 = (int64_t)blockIdx.x * p.rows_per_block;
-    const int64_t two_c = 2 * p.c;
+    for (int rr = threadIdx.x; rr < p.rows_per_block; rr += NT) {
+        const int64_t row = row0 + rr;
+        if (row < p.rows_total) {
+            int64_t r, n, j, src, ps;
+            split_row(row, p.b, p.tloc, r, n, j);
+            source_row(p.tab, p.cp, r, j, src, ps);
+            srow[rr] = n * p.s + src;
+        }
+    }
+    __syncthreads();
     const int nvec = p.rows_per_block * p.vecs_per_row;
     for (int i = threadIdx.x; i < nvec; i += NT) {
         const int rr = i / p.vecs_per_row;
         const int vv = i - rr * p.vecs_per_row;
         const int64_t row = row0 + rr;
         if (row >= p.rows_total) break;
-        int64_t r, n, j;
-        split_row(row, p.b, two_c, r, n, j);
-        const int64_t src_row = n * p.s + global_pos(r, j, p.c, p.cp);
-        const u32x4 *src = (const u32x4 *)p.x + src_row * p.vecs_per_row + vv;
+        const u32x4 *src = (const u32x4 *)p.x + srow[rr] * p.vecs_per_row + vv;
         u32x4 *dst = (u32x4 *)p.xz + row * p.vecs_per_row + vv;
         *dst = *src;
     }
-    if (p.pos != nullptr && blockIdx.x == 0) {
-        // positions of every rank: pos[r*2c + j]
-        const int64_t total = (int64_t)p.cp * two_c;
-        for (int64_t i = threadIdx.x; i < total; i += NT)
-            p.pos[i] = (int32_t)global_pos(i / two_c, i % two_c, p.c, p.cp);
-    }
+    if (p.pos != nullptr && blockIdx.x == 0) write_positions(p.tab, p.cp, p.tloc, p.pos);
 }
 
 template <typename T>
@@ -82,9 +111,10 @@ struct RopeParams {
     const T *x;
     T *xz;
     int32_t *pos;
-    int64_t s, c, b, rows_total;
+    int64_t s, tloc, b, rows_total;
     int cp, h, d;
     double theta;
+    SeqTable tab;
 };
 
 template <typename T>
@@ -110,11 +140,10 @@ template <typename T>
 __global__ void __launch_bounds__(NT) partition_rope(RopeParams<T> p) {
     extern __shared__ float cs[];   // [d/2] cos, then [d/2] sin
     const int half = p.d / 2;
-    const int64_t two_c = 2 * p.c;
     for (int64_t row = blockIdx.x; row < p.rows_total; row += gridDim.x) {
-        int64_t r, n, j;
-        split_row(row, p.b, two_c, r, n, j);
-        const int64_t gp = global_pos(r, j, p.c, p.cp);
+        int64_t r, n, j, sp, gp;
+        split_row(row, p.b, p.tloc, r, n, j);
+        source_row(p.tab, p.cp, r, j, sp, gp);
         __syncthreads();
         for (int t = threadIdx.x; t < half; t += NT) {
             const double inv_freq = pow(p.theta, -2.0 * (double)t / (double)p.d);
@@ -124,7 +153,7 @@ __global__ void __launch_bounds__(NT) partition_rope(RopeParams<T> p) {
             cs[half + t] = (float)sn;
         }
         __syncthreads();
-        const T *src = p.x + (n * p.s + gp) * (int64_t)p.h * p.d;
+        const T *src = p.x + (n * p.s + sp) * (int64_t)p.h * p.d;
         T *dst = p.xz + row * (int64_t)p.h * p.d;
         for (int i = threadIdx.x; i < p.h * half; i += NT) {
             const int hh = i / half, t = i - hh * half;
@@ -135,34 +164,33 @@ __global__ void __launch_bounds__(NT) partition_rope(RopeParams<T> p) {
             dst[hh * p.d + half + t] = from_f32<T>(x2 * cn + x1 * sn);
         }
     }
-    if (p.pos != nullptr && blockIdx.x == 0) {
-        const int64_t total = (int64_t)p.cp * two_c;
-        for (int64_t i = threadIdx.x; i < total; i += NT)
-            p.pos[i] = (int32_t)global_pos(i / two_c, i % two_c, p.c, p.cp);
-    }
+    if (p.pos != nullptr && blockIdx.x == 0) write_positions(p.tab, p.cp, p.tloc, p.pos);
 }
 
 }  // namespace
 
-hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const void *x,
-                            void *xz, int32_t *pos, const cpattn_rope *rope,
+hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const SeqTable &tab,
+                            const void *x, void *xz, int32_t *pos, const cpattn_rope *rope,
                             hipStream_t stream) {
     const int es = dtype == CPATTN_BF16 ? 2 : 4;
-    const int64_t c = dims.s / (2 * dims.cp);
-    const int64_t rows_total = (int64_t)dims.cp * dims.b * 2 * c;
+    const int64_t tloc = dims.s / dims.cp;
+    const int64_t rows_total = (int64_t)dims.cp * dims.b * tloc;
     if (rope == nullptr) {
         CopyParams p;
         p.x = (const char *)x;
         p.xz = (char *)xz;
         p.pos = pos;
         p.s = dims.s;
-        p.c = c;
+        p.tloc = tloc;
         p.b = dims.b;
         p.rows_total = rows_total;
         p.cp = dims.cp;
         p.vecs_per_row = (int)((int64_t)h * dims.d * es / 16);
-        // about 64 KiB per workgroup
+        p.tab = tab;
+        // about 64 KiB per workgroup (d >= 64 and es >= 2 give at least 8
+        // vectors per row, so at most MAX_ROWS_PER_BLOCK rows)
         p.rows_per_block = p.vecs_per_row >= 4096 ? 1 : 4096 / p.vecs_per_row;
+        if (p.rows_per_block > MAX_ROWS_PER_BLOCK) return hipErrorInvalidValue;
         const int64_t blocks = (rows_total + p.rows_per_block - 1) / p.rows_per_block;
         hipLaunchKernelGGL(partition_copy, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
         return hipGetLastError();
@@ -170,13 +198,13 @@ hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const voi
     const int64_t blocks = rows_total < 65536 ? rows_total : 65536;
     const size_t shmem = sizeof(float) * dims.d;
     if (dtype == CPATTN_BF16) {
-        RopeParams<uint16_t> p{(const uint16_t *)x, (uint16_t *)xz, pos, dims.s, c, dims.b,
-                               rows_total, dims.cp, h, dims.d, rope->theta};
+        RopeParams<uint16_t> p{(const uint16_t *)x, (uint16_t *)xz, pos, dims.s, tloc, dims.b,
+                               rows_total, dims.cp, h, dims.d, rope->theta, tab};
         hipLaunchKernelGGL(partition_rope<uint16_t>, dim3((unsigned)blocks), dim3(NT), shmem,
                            stream, p);
     } else {
-        RopeParams<float> p{(const float *)x, (float *)xz, pos, dims.s, c, dims.b,
-                            rows_total, dims.cp, h, dims.d, rope->theta};
+        RopeParams<float> p{(const float *)x, (float *)xz, pos, dims.s, tloc, dims.b,
+                            rows_total, dims.cp, h, dims.d, rope->theta, tab};
         hipLaunchKernelGGL(partition_rope<float>, dim3((unsigned)blocks), dim3(NT), shmem,
                            stream, p);
     }

@@ -28,8 +28,13 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 class CPProblem:
-    def __init__(self, w: Workload, q, k, v, s=None, device="cuda"):
+    """cu_seqlens: optional packing offsets (host, nseq + 1 entries): the
+    batch elements then pack independent samples, each split on its own
+    (cpattn_partition_varlen, cpattn_forward_fused_varlen)."""
+
+    def __init__(self, w: Workload, q, k, v, s=None, device="cuda", cu_seqlens=None):
         self.w = w
+        self.cu = None if cu_seqlens is None else np.asarray(cu_seqlens, dtype=np.int64)
         self.s = w.s if s is None else s
         self.b = q.shape[0]
         self.cp = w.cp
@@ -52,6 +57,13 @@ class CPProblem:
     # --- step 1: split -----------------------------------------------------
     def partition(self, stream=None):
         theta = self.w.rope_theta
+        if self.cu is not None:
+            for h, x, xz, pos, th in ((self.w.hq, self.q, self.qz, self.pos, theta),
+                                      (self.w.hkv, self.k, self.kz, None, theta),
+                                      (self.w.hkv, self.v, self.vz, None, None)):
+                C.cpattn_partition_varlen(self.dims, self.dtype, h, self.cu, x, xz, pos, th,
+                                          stream)
+            return
         C.cpattn_partition(self.dims, self.dtype, self.w.hq, self.q, self.qz, self.pos,
                            theta, stream)
         C.cpattn_partition(self.dims, self.dtype, self.w.hkv, self.k, self.kz, None,
@@ -116,6 +128,11 @@ class CPProblem:
 
     def forward_fused(self, out, stream=None, scale=0.0, with_lse=True):
         """The whole share through cpattn_forward_fused (one launch)."""
+        if self.cu is not None:
+            C.cpattn_forward_fused_varlen(self.dims, self.dtype, scale, out["rank"], self.cu,
+                                          self.qz, self.kz, self.vz, out["out_dtype"],
+                                          out["o"], out["lse"] if with_lse else None, stream)
+            return
         C.cpattn_forward_fused(self.dims, self.dtype, scale, out["rank"], self.qz, self.kz,
                                self.vz, out["out_dtype"], out["o"],
                                out["lse"] if with_lse else None, stream)

@@ -190,3 +190,72 @@ def test_forward_fused_validation_before_launch():
     bad_shape = list(args)
     bad_shape[0] = ctypes.byref(bad_s)
     assert L.cpattn_forward_fused(*bad_shape) == C.CPATTN_ESHAPE
+
+
+# --- packed variable-length samples ---------------------------------------
+
+from oracle import varlen as ovl  # noqa: E402
+
+
+@pytest.mark.parametrize("cu,cp", [([0, 8, 24, 32], 2), ([0, 6, 12, 30], 3),
+                                   ([0, 16, 32, 48, 64, 128], 8), ([0, 32768], 8),
+                                   ([0, 4096, 6144, 32768], 8)])
+def test_positions_varlen_bit_exact_vs_oracle(cu, cp):
+    s = cu[-1]
+    for r in range(cp):
+        got = C.cpattn_partition_positions_varlen(s, cp, r, cu)
+        assert got.dtype == np.int32
+        assert np.array_equal(got, ovl.local_positions(cu, cp, r))
+    # no offsets: the unpacked positions
+    out = np.empty(s // cp, dtype=np.int32)
+    assert C.lib().cpattn_partition_positions_varlen(
+        s, cp, 0, None, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == C.CPATTN_OK
+    assert np.array_equal(out, ocp.zigzag_positions(s, cp, 0))
+
+
+def _vl_status(cu, s=32, cp=2, nseq=None):
+    vl, keep = C.make_varlen(cu)
+    if nseq is not None:
+        vl.nseq = nseq
+    out = np.empty(s // cp, dtype=np.int32)
+    st = C.lib().cpattn_partition_positions_varlen(
+        s, cp, 0, ctypes.byref(vl), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    del keep
+    return st
+
+
+def test_varlen_offsets_rejected():
+    assert _vl_status([0, 8, 32]) == C.CPATTN_OK
+    assert _vl_status([0, 6, 32]) == C.CPATTN_ESHAPE        # 6 % 2cp
+    assert _vl_status([0, 8, 8, 32]) == C.CPATTN_ESHAPE     # empty sample
+    assert _vl_status([4, 8, 32]) == C.CPATTN_ESHAPE        # not from 0
+    assert _vl_status([0, 8, 28]) == C.CPATTN_ESHAPE        # not to s
+    assert _vl_status([0, 8, 32], nseq=0) == C.CPATTN_ESHAPE
+    many = list(range(0, 4 * 130, 4))
+    assert _vl_status(many, s=many[-1], nseq=129) == C.CPATTN_ESHAPE   # > CPATTN_MAX_SEQS
+    null_cu = C.cpattn_varlen(2, None)
+    out = np.empty(16, dtype=np.int32)
+    assert C.lib().cpattn_partition_positions_varlen(
+        32, 2, 0, ctypes.byref(null_cu),
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == C.CPATTN_EINVAL
+
+
+def test_varlen_device_calls_validate_before_launch():
+    L = C.lib()
+    d = _dims(b=1, s=4096, hq=8, hkv=2, d=128, cp=4)
+    bad, keep = C.make_varlen([0, 100, 4096])                # 100 % 8 != 0
+    good, keep2 = C.make_varlen([0, 1024, 4096])
+    assert L.cpattn_partition_varlen(ctypes.byref(d), 1, 8, ctypes.byref(bad), ALIGNED,
+                                     ALIGNED, None, None, 0) == C.CPATTN_ESHAPE
+    assert L.cpattn_partition_varlen(ctypes.byref(d), 1, 8, ctypes.byref(good), ALIGNED + 8,
+                                     ALIGNED, None, None, 0) == C.CPATTN_EALIGN
+    args = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), 1, ctypes.byref(bad), ALIGNED,
+            ALIGNED, ALIGNED, C.CPATTN_F32, ALIGNED, None, 0]
+    assert L.cpattn_forward_fused_varlen(*args) == C.CPATTN_ESHAPE
+    args[4] = ctypes.byref(good)
+    args[1] = C.CPATTN_F32
+    assert L.cpattn_forward_fused_varlen(*args) == C.CPATTN_EDTYPE
+    args[1] = C.CPATTN_BF16
+    args[3] = 4                                               # rank out of range
+    assert L.cpattn_forward_fused_varlen(*args) == C.CPATTN_EINVAL
+    del keep, keep2

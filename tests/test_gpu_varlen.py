@@ -1,0 +1,164 @@
+"""GPU packed variable-length samples (cpattn_partition_varlen,
+cpattn_forward_fused_varlen) vs the packed oracle (``oracle/varlen.py``:
+independent causal samples, each split by the zigzag rule on its own, RoPE
+at in-sample positions).
+
+* split: bit-exact bytes and in-sample positions for mixed sample lengths
+  (chunks of one row up to several tiles), fp32 and bf16; RoPE rows within
+  one bf16 rounding of the oracle's fp64 rotation at the in-sample positions;
+* fused forward at reduced lengths: every rank, row and head vs the packed
+  definition (GQA, MHA with wide logits, RoPE, b = 2), sample mixes whose
+  chunks straddle, fill and undershoot the 256-row query tiles;
+* one sample is bit-identical to the unpacked cpattn_forward_fused;
+* the headline dims packed into samples of 1k..22k rows: sampled rows of
+  the measured rank vs the oracle's rows of their sample.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from gpu_helpers import (BF16_MAX_ABS, BF16_MEAN_ABS, C, CPProblem, as_f32, assert_close,
+                         host_f32, make_inputs, say, small, torch)
+from long_context_causal_amd.inputs import WORKLOADS
+from long_context_causal_amd.runner import bf16_bits
+from oracle import attention_rows
+from oracle import cp as ocp
+from oracle import varlen as ovl
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.cpu().numpy().view(np.uint32)
+
+
+def _host_bits(x):
+    return x if x.dtype == np.uint16 else x.view(np.uint32)
+
+
+def _cu(cp, chunks):
+    """Offsets of samples whose chunk lengths are ``chunks``."""
+    return np.concatenate([[0], np.cumsum([2 * cp * c for c in chunks])]).astype(np.int64)
+
+
+SPLITS = [("fp32_mha_s512_cp2", [3, 60, 1, 64]),
+          ("bf16_gqa_s8k_cp4", [100, 1, 37, 256]),
+          ("bf16_gqa_s32k_cp8", [3, 17, 1, 40])]
+
+
+@pytest.mark.parametrize("name,chunks", SPLITS)
+def test_partition_varlen_bit_exact(name, chunks):
+    base = WORKLOADS[name]
+    cu = _cu(base.cp, chunks)
+    w = dataclasses.replace(small(base, int(cu[-1])), rope_theta=None)
+    say(f"partition varlen {name} cu={cu.tolist()}")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v, cu_seqlens=cu)
+    P.partition()
+    torch.cuda.synchronize()
+    for r in range(w.cp):
+        assert np.array_equal(P.pos[r].cpu().numpy(), ovl.local_positions(cu, w.cp, r))
+    for host, dev in ((k, P.kz), (v, P.vz), (q, P.qz)):
+        assert np.array_equal(_bits(dev), ovl.partition(_host_bits(host), cu, w.cp))
+
+
+def test_partition_varlen_rope_in_sample_positions():
+    base = WORKLOADS["bf16_gqa_s128k_cp16_rope"]
+    cp = 4
+    cu = _cu(cp, [5, 64, 1, 130])
+    w = dataclasses.replace(base, s=int(cu[-1]), cp=cp)
+    say(f"partition varlen + rope cu={cu.tolist()}")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v, cu_seqlens=cu)
+    P.partition()
+    torch.cuda.synchronize()
+    qz, kz = host_f32(P.qz), host_f32(P.kz)
+    for r in range(cp):
+        rows, pos = ovl.local_rows(cu, cp, r), ovl.local_positions(cu, cp, r)
+        for nm, host, dev in (("q", q, qz), ("k", k, kz)):
+            want = ocp.rope(as_f32(host[:, rows]).astype(np.float64), pos, w.rope_theta)
+            err = np.abs(dev[r] - want)
+            bound = np.abs(want) * 2.0 ** -8 + 1e-6
+            say(f"  rank {r} {nm}: max err/bound {float((err / bound).max()):.3f}")
+            assert np.all(err <= bound)
+    assert np.array_equal(_bits(P.vz), ovl.partition(_host_bits(v), cu, cp))
+
+
+def _packed_ref(w, q, k, v, cu):
+    qf, kf, vf = (as_f32(x).astype(np.float64) for x in (q, k, v))
+    return ovl.packed_causal_attention(qf, kf, vf, cu, rope_theta=w.rope_theta)
+
+
+def run_fused(P, rank):
+    out = P.alloc_out(rank, C.CPATTN_F32)
+    P.forward_fused(out)
+    torch.cuda.synchronize()
+    return host_f32(out["o"]), out["lse"].cpu().numpy()
+
+
+FUSED = [("bf16_gqa_s8k_cp4", [100, 1, 37, 256, 64], None),
+         ("bf16_gqa_s32k_cp8", [40, 130, 3], 2),
+         ("bf16_mha_s16k_cp4_widelogits", [96, 200, 5], None),
+         ("bf16_gqa_s128k_cp16_rope", [24, 7, 65], None)]
+
+
+@pytest.mark.parametrize("name,chunks,b", FUSED)
+def test_fused_varlen_reduced_all_ranks(name, chunks, b):
+    base = WORKLOADS[name]
+    cu = _cu(base.cp, chunks)
+    w = small(base, int(cu[-1]), b)
+    say(f"fused varlen {name} cu={cu.tolist()} b={w.b}")
+    q, k, v = make_inputs(w)
+    o_ref, l_ref = _packed_ref(w, q, k, v, cu)
+    P = CPProblem(w, q, k, v, cu_seqlens=cu)
+    P.partition()
+    for r in range(w.cp):
+        o, l = run_fused(P, r)
+        rows = ovl.local_rows(cu, w.cp, r)
+        assert_close(f"rank {r} O", o, o_ref[:, rows], BF16_MAX_ABS, BF16_MEAN_ABS)
+        assert_close(f"rank {r} L", l, l_ref[:, :, rows], 1e-3)
+
+
+def test_fused_varlen_one_sample_is_unpacked():
+    w = small(WORKLOADS["bf16_gqa_s32k_cp8"], 2 * 8 * 300)
+    say("fused varlen, one sample")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    Pv = CPProblem(w, q, k, v, cu_seqlens=[0, w.s])
+    Pv.partition()
+    torch.cuda.synchronize()
+    assert torch.equal(P.qz, Pv.qz) and torch.equal(P.kz, Pv.kz)
+    for r in (0, w.rank, w.cp - 1):
+        o, l = run_fused(P, r)
+        ov, lv = run_fused(Pv, r)
+        assert np.array_equal(o, ov) and np.array_equal(l, lv)
+
+
+def test_fused_varlen_full_size_sampled_rows():
+    w = WORKLOADS["bf16_gqa_s32k_cp8"]
+    cp, r = w.cp, w.rank
+    cu = np.array([0, 1024, 9216, 10240, 32768], dtype=np.int64)
+    say(f"fused varlen full size {w.name} cu={cu.tolist()} rank {r}")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v, cu_seqlens=cu)
+    P.partition()
+    o, l = run_fused(P, r)
+    rows = ovl.local_rows(cu, cp, r)
+    rng = np.random.default_rng(3)
+    for i in range(len(cu) - 1):
+        a, e = cu[i] // cp, cu[i + 1] // cp
+        pick = np.unique(np.concatenate([[a, a + (e - a) // 2 - 1, a + (e - a) // 2, e - 1],
+                                         rng.integers(a, e, 6)]))
+        g = rows[pick]                          # packed rows of the picked local rows
+        s0 = int(cu[i])
+        qf = as_f32(q[:, g]).astype(np.float64)
+        hi = int(g.max()) + 1
+        kf = as_f32(k[:, s0:hi]).astype(np.float64)
+        vf = as_f32(v[:, s0:hi]).astype(np.float64)
+        o_ref, l_ref = attention_rows(qf, kf, vf, g - s0 + 1)
+        assert_close(f"sample {i} O", o[:, pick], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+        assert_close(f"sample {i} L", l[:, :, pick], l_ref, 1e-3)

@@ -21,6 +21,7 @@ The CPU baseline times the fp64 oracle on the host cores on a bounded
 sample of the same rank share (every k-th local row, all heads).
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -48,6 +49,17 @@ def parse():
 # the sources the forward attention kernels are built from (their digest
 # ties a committed counter summary to the code it was measured on)
 KERNEL_SOURCES = ("attn_step_bf16.hip", "mfma_tiles.h")
+
+
+def packing_offsets(s, cp):
+    """Sample offsets of the packed leg: eight samples in the length ratio
+    1:2:4:1:8:3:5:8 (units of s/32 rows, each a multiple of 2cp)."""
+    import numpy as np
+    units = [1, 2, 4, 1, 8, 3, 5, 8]
+    unit = s // 32
+    if unit % (2 * cp) != 0 or unit * 32 != s:
+        raise ValueError("the packed leg needs s/32 to be a multiple of 2*cp")
+    return np.concatenate([[0], np.cumsum([u * unit for u in units])]).astype(np.int64)
 
 
 def committed_traffic(workload, key="attention_traffic_bytes_per_launch"):
@@ -184,6 +196,38 @@ def main():
         fused = {"ms": float(np.mean([a.elapsed_time(b) for a, b in f_total])),
                  "attn_ms": float(np.mean([a.elapsed_time(b) for a, b in f_attn]))}
 
+    # the same dims packed into samples of mixed lengths (each an independent
+    # causal sequence split on its own): split, then one varlen launch
+    varlen = None
+    if w.dtype == "bf16":
+        cu = packing_offsets(w.s, w.cp)
+        Pv = CPProblem(w, P.q, P.k, P.v, cu_seqlens=cu)
+        vout = Pv.alloc_out(rank, C.CPATTN_F32)
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                Pv.partition(stream)
+                Pv.forward_fused(vout, stream)
+            torch.cuda.synchronize()
+            v_total, v_attn = [], []
+            for _ in range(args.steps):
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record(stream)
+                Pv.partition(stream)
+                e1.record(stream)
+                Pv.forward_fused(vout, stream)
+                e2.record(stream)
+                v_total.append((e0, e2))
+                v_attn.append((e1, e2))
+            torch.cuda.synchronize()
+        # each sample's rank share: 4*d per visible pair, c(2c+1) + (cp-1)*2c^2
+        # pairs per (batch, head) with c the sample's chunk length
+        v_flops = sum(dataclasses.replace(w, s=int(cu[i + 1] - cu[i])).rank_flops()
+                      for i in range(len(cu) - 1))
+        varlen = {"cu": cu, "flops": v_flops,
+                  "ms": float(np.mean([a.elapsed_time(b) for a, b in v_total])),
+                  "attn_ms": float(np.mean([a.elapsed_time(b) for a, b in v_attn]))}
+        del Pv, vout
+
     # the backward of the same share: dO seeded bf16, the rank's merged O
     # and L from the forward above
     backward = None
@@ -276,6 +320,19 @@ def main():
             "achieved": round(f_tf, 2),
             "frac": round(f_tf / peak, 4),
             "traffic": committed_traffic(w.name, "fused_traffic_bytes_per_launch"),
+        }
+    if varlen is not None:
+        cu = varlen["cu"]
+        v_tf = varlen["flops"] / (varlen["attn_ms"] * 1e-3) / 1e12
+        line["varlen"] = {
+            "entry_point": "cpattn_forward_fused_varlen",
+            "sample_lengths": [int(cu[i + 1] - cu[i]) for i in range(len(cu) - 1)],
+            "flops": varlen["flops"],
+            "ms_per_step": round(varlen["ms"], 4),
+            "value": round(varlen["flops"] / (varlen["ms"] * 1e-3) / 1e12, 2),
+            "avg_launch_ms": round(varlen["attn_ms"], 4),
+            "achieved": round(v_tf, 2),
+            "frac": round(v_tf / peak, 4),
         }
     if backward is not None:
         b_flops = 2.5 * flops

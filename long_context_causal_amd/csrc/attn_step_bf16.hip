@@ -215,8 +215,10 @@ struct Kernel {
         f32x16 s[2];             // S^T of the tile between its two phases
         bf16x8 pf[BN / 16];      // P of the tile between its two phases
         float m_run, l_run;
-        unsigned koff[D / 16];   // lane's byte offset of each K chunk in a stage
-        unsigned voff[D / 32];   // lane's byte offset of each V^T read in a stage
+        // lane's LDS address of each K chunk / V^T read in the current
+        // stages (advanced once per tile, so matrix phases add immediates only)
+        unsigned koff[D / 16];
+        unsigned voff[D / 32];
         unsigned gk[KI], gv[KI]; // lane's byte offsets of its K and V copies in a tile
         int krow[KI];            // tile row of each of the lane's copies
         int64_t kstride;         // elements between consecutive keys
@@ -253,11 +255,11 @@ struct Kernel {
         }
     }
 
-    // Matrix phase: S^T(t) = K(t) Q^T and O^T += V(t-1)^T P(t-1).  sK: stage
-    // of tile t, sV: V tile of tile t-1.  One code path for every phase: the
+    // Matrix phase: S^T(t) = K(t) Q^T and O^T += V(t-1)^T P(t-1), from the
+    // stages S.koff / S.voff point at.  One code path for every phase: the
     // first phase multiplies a zeroed V tile by P = 0, and the S^T of the
     // phase after a wave's last tile is computed on resident rows and dropped.
-    __device__ __forceinline__ static void matrix_phase(State &S, unsigned sK, unsigned sV) {
+    __device__ __forceinline__ static void matrix_phase(State &S) {
         // Eight steps of four MFMAs: step i does k-step i of S^T (both 32-key
         // halves) and head-dim tiles 2(i%2), 2(i%2)+1 of key chunk i/2 of O^T.
         // The LDS reads of step i+2 are issued before the MFMAs of step i, so
@@ -265,11 +267,11 @@ struct Kernel {
         // the compiler from hoisting every read, which would exhaust registers).
         bf16x8 kf[3][2], vf[3][2];
         auto reads = [&](int i, int slot) {
-            kf[slot][0] = k_read(sK + S.koff[i]);
-            kf[slot][1] = k_read(sK + S.koff[i] + 32 * ROWB);
+            kf[slot][0] = k_read(S.koff[i]);
+            kf[slot][1] = k_read(S.koff[i] + 32 * ROWB);
             const int kc = i >> 1, dt0 = 2 * (i & 1);
-            vf[slot][0] = vt_read(sV + S.voff[dt0] + kc * 16 * ROWB);
-            vf[slot][1] = vt_read(sV + S.voff[dt0 + 1] + kc * 16 * ROWB);
+            vf[slot][0] = vt_read(S.voff[dt0] + kc * 16 * ROWB);
+            vf[slot][1] = vt_read(S.voff[dt0 + 1] + kc * 16 * ROWB);
         };
         reads(0, 0);
         reads(1, 1);
@@ -445,6 +447,10 @@ struct Kernel {
         }
         const unsigned lds_addr =
             (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) S.koff[kk] += lds_addr;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) S.voff[dt] += lds_addr + (NS - 1) * 2 * TILEB + TILEB;
         // prologue: tiles 0 and 1 in flight, then Q; one full wait before the
         // loop (tile 0 has to land first anyway) also tells the compiler that
         // Q is resident, so it puts no memory wait inside the loop
@@ -475,8 +481,7 @@ struct Kernel {
             const int hg = 2 * t + grp;
             sync(P, S, hg, lds_addr, wave);
             if (P.comp(t, wrow0) || P.comp(t - 1, wrow0))
-                matrix_phase(S, lds_addr + (t % NS) * 2 * TILEB,
-                             lds_addr + ((t + NS - 1) % NS) * 2 * TILEB + TILEB);
+                matrix_phase(S);
             if (t == ntiles) break;
             sync(P, S, hg + 1, lds_addr, wave);
             if (P.comp(t, wrow0)) {
@@ -486,6 +491,17 @@ struct Kernel {
                 for (int kc = 0; kc < BN / 16; ++kc)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) S.pf[kc][e] = (__bf16)0.0f;
+            }
+            {   // next tile, in the vector half: the K stage moves from t % NS to
+                // (t+1) % NS and the V stage from (t-1) % NS to t % NS
+                const unsigned kstep = ((t + 1) % NS == 0) ? (unsigned)(-(NS - 1) * 2 * TILEB)
+                                                           : (unsigned)(2 * TILEB);
+                const unsigned vstep = (t % NS == 0) ? (unsigned)(-(NS - 1) * 2 * TILEB)
+                                                     : (unsigned)(2 * TILEB);
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) S.koff[kk] += kstep;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) S.voff[dt] += vstep;
             }
         }
         if (grp == 0) sync(P, S, 2 * ntiles + 1, lds_addr, wave);

@@ -15,7 +15,9 @@ forward's merged O and L) under "backward".
 
 value = causal-effective FLOPs of the rank's share (4*d per visible query/
 key pair) / the measured time of a step.  Per-kernel times come from HIP
-events recorded on the stream the kernels run on.
+events recorded on the stream the kernels run on.  Also reported: the step
+kernels' TFLOP/s for every rank of the share ("ranks", min and max), and
+for the other bf16 configurations at their measured rank ("configs").
 
 The CPU baseline times the fp64 oracle on the host cores on a bounded
 sample of the same rank share (every k-th local row, all heads).
@@ -43,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the per-rank and per-configuration step timings")
     return ap.parse_args()
 
 
@@ -122,6 +126,35 @@ def cpu_baseline(w, q, k, v, rank, target_s):
             "sample": f"rank {rank}: every {stride}th of its {len(pos_all)} local rows "
                       f"({len(sample)} rows x {w.hq} heads x b={w.b}, all visible keys), "
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64"}
+
+
+def share_step_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
+    """(attention TFLOP/s over the summed step-kernel times, TFLOP/s over
+    steps + merge) of one rank's share, from HIP events on ``stream``."""
+    import numpy as np
+    buf = P.alloc_rank(rank, C.CPATTN_F32)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            for i in range(w.cp):
+                P.step(buf, i, stream)
+            P.merge(buf, stream)
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            for i in range(w.cp):
+                P.step(buf, i, stream)
+            e[1].record(stream)
+            P.merge(buf, stream)
+            e[2].record(stream)
+            ev.append(e)
+        torch.cuda.synchronize()
+    steps = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    whole = float(np.median([a.elapsed_time(c) for a, _, c in ev]))
+    flops = w.rank_flops()
+    del buf
+    return flops / (steps * 1e-3) / 1e12, flops / (whole * 1e-3) / 1e12
 
 
 def main():
@@ -345,6 +378,27 @@ def main():
             "value": round(b_tf, 2),
             "frac": round(b_tf / peak, 4),
         }
+    # every rank of the headline share (the step kernels' TFLOP/s), and the
+    # other bf16 configurations at their measured rank
+    if w.dtype == "bf16" and not args.no_extra:
+        per_rank = [share_step_tflops(C, torch, P, w, r, stream)[0] for r in range(w.cp)]
+        line["ranks"] = {"attention_tflops_min": round(min(per_rank), 2),
+                         "attention_tflops_max": round(max(per_rank), 2),
+                         "attention_tflops": [round(x, 1) for x in per_rank]}
+        configs = {}
+        for name in ("bf16_gqa_s8k_cp4", "bf16_mha_s16k_cp4_widelogits",
+                     "bf16_gqa_s128k_cp16_rope"):
+            wc = WORKLOADS[name]
+            Pc = CPProblem(wc, *make_inputs(wc))
+            with torch.cuda.stream(stream):
+                Pc.partition(stream)
+            a_tf, w_tf = share_step_tflops(C, torch, Pc, wc, wc.rank, stream)
+            configs[name] = {"rank": wc.rank, "attention_tflops": round(a_tf, 2),
+                             "frac": round(a_tf / peak, 4),
+                             "steps_plus_merge_tflops": round(w_tf, 2)}
+            del Pc
+            torch.cuda.empty_cache()
+        line["configs"] = configs
     if args.cpu_sample_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, rank, args.cpu_sample_seconds)
     else:

@@ -28,7 +28,7 @@ new arithmetic.
 """
 import numpy as np
 
-from .attention import attention_rows
+from .attention import attention_rows, attention_rows_bwd
 from . import cp as ocp
 
 
@@ -120,3 +120,40 @@ def cp_forward_rank(q, k, v, cu, cp, rank, scale=None, rope_theta=None, nthreads
         os_.append(o_i)
         ls_.append(l_i)
     return np.concatenate(os_, axis=1), np.concatenate(ls_, axis=2)
+
+
+def packed_causal_attention_bwd(q, k, v, dout, cu, scale=None, nthreads=0):
+    """Gradients of the packed definition (no RoPE: with respect to the
+    attention inputs): each sample's causal-attention gradients on its own
+    rows.  Returns (dq [b, s, hq, d], dk, dv [b, s, hkv, d])."""
+    cu = np.asarray(cu, dtype=np.int64)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for i in range(cu.size - 1):
+        a, e = int(cu[i]), int(cu[i + 1])
+        dq[:, a:e], dk[:, a:e], dv[:, a:e] = attention_rows_bwd(
+            q[:, a:e], k[:, a:e], v[:, a:e], dout[:, a:e], np.arange(1, e - a + 1), scale,
+            nthreads)
+    return dq, dk, dv
+
+
+def cp_backward_rank(q, k, v, dout, cu, cp, rank, scale=None, nthreads=0):
+    """One rank's CP backward share of a packed batch (no RoPE).
+
+    Sample by sample, the single-sequence CP backward (the rank's final L and
+    D of that sample, the cp ring steps); the rank's dq and its contributions
+    to every rank's dK/dV are laid out in local row order.  Returns
+    (dq_r [b, s/cp, hq, d], dkz, dvz [cp, b, s/cp, hkv, d]).
+    """
+    cu = np.asarray(cu, dtype=np.int64)
+    dqs, dks, dvs = [], [], []
+    for i in range(cu.size - 1):
+        a, e = int(cu[i]), int(cu[i + 1])
+        dq_i, dk_i, dv_i = ocp.cp_backward_rank(q[:, a:e], k[:, a:e], v[:, a:e], dout[:, a:e],
+                                                cp, rank, scale, nthreads=nthreads)
+        dqs.append(dq_i)
+        dks.append(dk_i)
+        dvs.append(dv_i)
+    return (np.concatenate(dqs, axis=1), np.concatenate(dks, axis=2),
+            np.concatenate(dvs, axis=2))

@@ -18,7 +18,10 @@ sample boundaries) are stated in ``oracle/varlen.py``.  Pinned here:
   definition, with and without RoPE, for mixed lengths down to one-row
   chunks (a split finer than any kernel tile);
 * RoPE depends only on position differences, so resetting positions at the
-  sample start gives the attention of the unreset (packed-index) positions.
+  sample start gives the attention of the unreset (packed-index) positions;
+* backward: central differences of a loss through the packed forward, and
+  the CP invariant (every rank's dq, and the ranks' dK/dV contributions
+  summed per owner, equal the packed gradients).
 """
 import numpy as np
 import pytest
@@ -159,3 +162,54 @@ def test_bad_offsets_rejected():
     with pytest.raises(ValueError):
         ovl.check_cu([4, 16], 16, 2)
     assert ovl.check_cu([0, 4, 16], 16, 2).dtype == np.int64
+
+
+# --- backward ----------------------------------------------------------------
+
+def test_bwd_finite_differences_of_packed_definition():
+    """Central differences of a scalar loss through the packed forward: a
+    check of the gradients that never calls the gradient code's per-sample
+    slicing on the forward side."""
+    rng = np.random.default_rng(21)
+    cu = [0, 4, 12]
+    q, k, v = _qkv(rng, 1, 12, 2, 1, 4, 0.8)
+    w_o = rng.standard_normal((1, 12, 2, 4))
+    dq, dk, dv = ovl.packed_causal_attention_bwd(q, k, v, w_o, cu, scale=0.6)
+
+    def loss(q_, k_, v_):
+        o, _ = ovl.packed_causal_attention(q_, k_, v_, cu, scale=0.6)
+        return float((o * w_o).sum())
+
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            num = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(num - g[idx]) <= 1e-6 * max(1.0, abs(num)), (name, idx, num, g[idx])
+
+
+@pytest.mark.parametrize("cu,cp", [([0, 8, 40, 48], 4), ([0, 12, 24, 60], 3)])
+def test_bwd_cp_invariant(cu, cp):
+    """The ranks' dq and their summed dK/dV contributions (what the
+    reduce-scatter forms on each owner) equal the packed gradients."""
+    rng = np.random.default_rng(cp + len(cu))
+    s = cu[-1]
+    q, k, v = _qkv(rng, 2, s, 4, 2, 8)
+    dout = rng.standard_normal(q.shape)
+    dq_ref, dk_ref, dv_ref = ovl.packed_causal_attention_bwd(q, k, v, dout, cu)
+    dkz_sum = np.zeros((cp, 2, s // cp, 2, 8))
+    dvz_sum = np.zeros_like(dkz_sum)
+    for r in range(cp):
+        dq_r, dkz, dvz = ovl.cp_backward_rank(q, k, v, dout, cu, cp, r)
+        np.testing.assert_allclose(dq_r, dq_ref[:, ovl.local_rows(cu, cp, r)], rtol=0,
+                                   atol=1e-11)
+        dkz_sum += dkz
+        dvz_sum += dvz
+    np.testing.assert_allclose(ovl.unpartition(dkz_sum, cu), dk_ref, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(ovl.unpartition(dvz_sum, cu), dv_ref, rtol=0, atol=1e-11)

@@ -276,6 +276,17 @@ int cpattn_forward_fused_varlen(const cpattn_dims *dims, int dtype, float scale,
                                 const void *vz, int out_dtype, void *o_out, float *lse_out,
                                 void *stream);
 
+/* cpattn_backward_varlen, device: cpattn_backward for a packed batch (see
+ * cpattn_varlen): every sample's rows take the backward of the cp ring
+ * steps of that sample only.  Buffers as cpattn_backward with 2c read as
+ * s/cp local rows; o_r and lse_r from cpattn_forward_fused_varlen.  vl =
+ * NULL gives cpattn_backward. */
+int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int rank,
+                           const cpattn_varlen *vl, const void *qz, const void *kz,
+                           const void *vz, const float *o_r, const void *do_r,
+                           const float *lse_r, float *delta_ws, float *dq_r, float *dkz,
+                           float *dvz, void *stream);
+
 /* Static name of a status code. */
 const char *cpattn_status_str(int status);
 

@@ -90,6 +90,8 @@ def lib():
         L.cpattn_partition_varlen.argtypes = [D, I, I, V, P, P, P, ctypes.POINTER(cpattn_rope), P]
         L.cpattn_forward_fused_varlen.argtypes = [D, I, ctypes.c_float, I, V, P, P, P, I, P, P,
                                                   P]
+        L.cpattn_backward_varlen.argtypes = [D, I, ctypes.c_float, I, V, P, P, P, P, P, P, P, P,
+                                             P, P, P]
         L.cpattn_bwd_delta.argtypes = [D, P, P, P, P]
         L.cpattn_step_bwd.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P]
         L.cpattn_backward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P, P]
@@ -99,7 +101,8 @@ def lib():
                      "cpattn_step_fwd", "cpattn_merge", "cpattn_forward",
                      "cpattn_forward_fused", "cpattn_bwd_delta", "cpattn_step_bwd",
                      "cpattn_backward", "cpattn_partition_positions_varlen",
-                     "cpattn_partition_varlen", "cpattn_forward_fused_varlen"):
+                     "cpattn_partition_varlen", "cpattn_forward_fused_varlen",
+                     "cpattn_backward_varlen"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -244,4 +247,15 @@ def cpattn_forward_fused_varlen(dims, dtype, scale, rank, cu_seqlens, qz, kz, vz
                                              out_dtype, _ptr(o_out), _ptr(lse_out),
                                              _stream(stream)),
            "cpattn_forward_fused_varlen")
+    del keep
+
+
+def cpattn_backward_varlen(dims, dtype, scale, rank, cu_seqlens, qz, kz, vz, o_r, do_r, lse_r,
+                           delta_ws, dq_r, dkz, dvz, stream=None):
+    vl, keep = make_varlen(cu_seqlens)
+    _check(lib().cpattn_backward_varlen(ctypes.byref(dims), dtype, float(scale), rank,
+                                        ctypes.byref(vl), _ptr(qz), _ptr(kz), _ptr(vz),
+                                        _ptr(o_r), _ptr(do_r), _ptr(lse_r), _ptr(delta_ws),
+                                        _ptr(dq_r), _ptr(dkz), _ptr(dvz), _stream(stream)),
+           "cpattn_backward_varlen")
     del keep

@@ -298,6 +298,7 @@ int cpattn_forward_fused_varlen(const cpattn_dims *dims, int dtype, float scale,
         return CPATTN_ESHAPE;
     if (rank < 0 || rank >= dims->cp) return CPATTN_EINVAL;
     if (!qz || !kz || !vz || !o_out) return CPATTN_EINVAL;
+    if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
     if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
     if (out_dtype != CPATTN_F32 && out_dtype != CPATTN_BF16) return CPATTN_EDTYPE;
     if (dims->d != 128) return CPATTN_ESHAPE;
@@ -348,6 +349,7 @@ int cpattn_step_bwd(const cpattn_dims *dims, int dtype, float scale, int mode, c
     if (mode < CPATTN_CAUSAL || mode > CPATTN_Q_SECOND_HALF) return CPATTN_EINVAL;
     if (!q_r || !k_src || !v_src || !do_r || !lse_r || !delta_r || !dq_r || !dk_src || !dv_src)
         return CPATTN_EINVAL;
+    if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
     if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
     if (dims->d != 128) return CPATTN_ESHAPE;
     if (!aligned16(q_r) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(do_r) ||
@@ -355,19 +357,27 @@ int cpattn_step_bwd(const cpattn_dims *dims, int dtype, float scale, int mode, c
         ((uintptr_t)lse_r & 3u) || ((uintptr_t)delta_r & 3u))
         return CPATTN_EALIGN;
     const StepGeom g = cpattn::step_geom(*dims, mode, scale);
-    return status_of(cpattn::launch_step_bwd_bf16(g, q_r, k_src, v_src, do_r, lse_r, delta_r,
-                                                  dq_r, dk_src, dv_src, (hipStream_t)stream));
+    cpattn::SeqTable t;
+    make_table(dims->s, dims->cp, nullptr, t);
+    return status_of(cpattn::launch_step_bwd_bf16(g, t, mode, q_r, k_src, v_src, do_r, lse_r,
+                                                  delta_r, dq_r, dk_src, dv_src,
+                                                  (hipStream_t)stream));
 }
 
-int cpattn_backward(const cpattn_dims *dims, int dtype, float scale, int rank, const void *qz,
-                    const void *kz, const void *vz, const float *o_r, const void *do_r,
-                    const float *lse_r, float *delta_ws, float *dq_r, float *dkz, float *dvz,
-                    void *stream) {
+int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int rank,
+                           const cpattn_varlen *vl, const void *qz, const void *kz,
+                           const void *vz, const float *o_r, const void *do_r,
+                           const float *lse_r, float *delta_ws, float *dq_r, float *dkz,
+                           float *dvz, void *stream) {
     int st = check_dims(dims);
+    if (st) return st;
+    cpattn::SeqTable t;
+    st = make_table(dims->s, dims->cp, vl, t);
     if (st) return st;
     if (rank < 0 || rank >= dims->cp) return CPATTN_EINVAL;
     if (!qz || !kz || !vz || !o_r || !do_r || !lse_r || !delta_ws || !dq_r || !dkz || !dvz)
         return CPATTN_EINVAL;
+    if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
     if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
     if (dims->d != 128) return CPATTN_ESHAPE;
     if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz) || !aligned16(o_r) ||
@@ -391,11 +401,20 @@ int cpattn_backward(const cpattn_dims *dims, int dtype, float scale, int rank, c
         // ring hand-off: step i reads rank src's K/V and adds to src's dK/dV
         const char *k_src = (const char *)kz + src * kv_elems * 2;
         const char *v_src = (const char *)vz + src * kv_elems * 2;
-        st = cpattn_step_bwd(dims, dtype, scale, mode, q_r, k_src, v_src, do_r, lse_r,
-                             delta_ws, dq_r, dkz + src * kv_elems, dvz + src * kv_elems, stream);
-        if (st) return st;
+        const StepGeom g = cpattn::step_geom(*dims, mode, scale);
+        e = cpattn::launch_step_bwd_bf16(g, t, mode, q_r, k_src, v_src, do_r, lse_r, delta_ws,
+                                         dq_r, dkz + src * kv_elems, dvz + src * kv_elems, s);
+        if (e != hipSuccess) return CPATTN_EHIP;
     }
     return CPATTN_OK;
+}
+
+int cpattn_backward(const cpattn_dims *dims, int dtype, float scale, int rank, const void *qz,
+                    const void *kz, const void *vz, const float *o_r, const void *do_r,
+                    const float *lse_r, float *delta_ws, float *dq_r, float *dkz, float *dvz,
+                    void *stream) {
+    return cpattn_backward_varlen(dims, dtype, scale, rank, nullptr, qz, kz, vz, o_r, do_r,
+                                  lse_r, delta_ws, dq_r, dkz, dvz, stream);
 }
 
 }  // extern "C"

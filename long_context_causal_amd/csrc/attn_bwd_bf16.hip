@@ -56,14 +56,34 @@ constexpr int TB = TR * RB;                // bytes per tile
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct BwdParams {
-    const uint16_t *q, *k, *v, *dout;   // q_r, dout_r [b, 2c, hq, d]; k, v [b, 2c, hkv, d]
-    const float *lse, *delta;           // the rank's final L (natural log) and D [b, hq, 2c]
-    float *dq, *dk, *dv;                // accumulated: dq [b, 2c, hq, d]; dk, dv [b, 2c, hkv, d]
-    int64_t two_c, q_row0;
-    int b, nq, nk, hq, hkv, group, ntiles_wg, head_splits;
+    const uint16_t *q, *k, *v, *dout;   // q_r, dout_r [b, T, hq, d]; k, v [b, T, hkv, d]
+    const float *lse, *delta;           // the rank's final L (natural log) and D [b, hq, T]
+    float *dq, *dk, *dv;                // accumulated: dq [b, T, hq, d]; dk, dv [b, T, hkv, d]
+    int64_t two_c;                      // T: local rows per batch element
+    int b, hq, hkv, group, head_splits;
     float scale, scale_log2;
-    int causal;
+    int mode;                           // the step's mode (same for every sample)
+    SeqTable tab;                       // packed samples; tile0: this kernel's tiles
 };
+
+// One sample's rows and keys in a step of the given mode: query rows
+// [qrow0, qrow0 + nq) and keys [kv0, kv0 + nk) of the local blocks (key j
+// visible to row i only if j <= i, both counted from the sample start, when
+// causal).
+struct Geo {
+    int qrow0, kv0, nq, nk;
+    bool causal;
+};
+__device__ __forceinline__ Geo geo_of(const BwdParams &p, int i) {
+    const int l0 = p.tab.lcu[i], c = (p.tab.lcu[i + 1] - l0) >> 1;
+    Geo G;
+    G.kv0 = l0;
+    G.causal = p.mode == CPATTN_CAUSAL;
+    G.qrow0 = p.mode == CPATTN_Q_SECOND_HALF ? l0 + c : l0;
+    G.nq = p.mode == CPATTN_Q_SECOND_HALF ? c : 2 * c;
+    G.nk = p.mode == CPATTN_KV_FIRST_HALF ? c : 2 * c;
+    return G;
+}
 
 __device__ __forceinline__ int u_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
@@ -171,17 +191,20 @@ attn_bwd_dq(BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
     int item = blockIdx.x;
-    const int nqt = p.ntiles_wg;
-    const int qt = nqt - 1 - item % nqt;       // longest (causal) tiles first
+    const int nqt = p.tab.tile0[p.tab.nseq];   // query tiles of all samples
+    const int qt_all = nqt - 1 - item % nqt;   // longest (causal) tiles first
     item /= nqt;
     const int head = item % p.hq;
     const int n = item / p.hq;
     const int g = head / p.group;
+    const int smp = seq_of(p.tab.tile0, p.tab.nseq, qt_all);
+    const Geo G = geo_of(p, smp);
+    const int qt = qt_all - p.tab.tile0[smp];
     const int q0 = qt * TR * NWB;
     const int wrow0 = q0 + wave * TR;
-    const int kend = p.causal ? min(p.nk, q0 + TR * NWB) : p.nk;
+    const int kend = G.causal ? min(G.nk, q0 + TR * NWB) : G.nk;
     const int ntiles = (kend + TR - 1) / TR;
-    const int wtiles = p.causal ? min(ntiles, (wrow0 + TR - 1) / TR + 1) : ntiles;
+    const int wtiles = G.causal ? min(ntiles, (wrow0 + TR - 1) / TR + 1) : ntiles;
 
     LaneOffsets L;
     L.init(lane);
@@ -189,12 +212,12 @@ attn_bwd_dq(BwdParams p) {
 
     // this lane's query row: Q and dO as B operands, L (log2) and D
     const int qrow = wrow0 + l32;
-    const int qr = min(qrow, p.nq - 1);
-    const int64_t qoff = ((n * p.two_c + p.q_row0 + qr) * (int64_t)p.hq + head) * D;
+    const int qr = min(qrow, G.nq - 1);
+    const int64_t qoff = ((n * p.two_c + G.qrow0 + qr) * (int64_t)p.hq + head) * D;
     bf16x8 qf[D / 16], df[D / 16];
     load_b_rows(p.q + qoff, hi, qf);
     load_b_rows(p.dout + qoff, hi, df);
-    const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + p.q_row0 + qr;
+    const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + G.qrow0 + qr;
     const float lq = p.lse[lrow] * LOG2E;
     const float dq_d = p.delta[lrow];
     settle(qf);
@@ -207,8 +230,8 @@ attn_bwd_dq(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
 
-    const uint16_t *kb = p.k + ((int64_t)n * p.two_c * p.hkv + g) * D;
-    const uint16_t *vb = p.v + ((int64_t)n * p.two_c * p.hkv + g) * D;
+    const uint16_t *kb = p.k + (((int64_t)n * p.two_c + G.kv0) * p.hkv + g) * D;
+    const uint16_t *vb = p.v + (((int64_t)n * p.two_c + G.kv0) * p.hkv + g) * D;
     const int64_t row_bytes = (int64_t)p.hkv * D * 2;
     const unsigned coff = copy_offset(lane, wave, row_bytes);   // m = wave, wave + 4
     // tiles past the last repeat it, so every wave issues 4 copies per tile
@@ -217,8 +240,8 @@ attn_bwd_dq(BwdParams p) {
         const unsigned sb = lbase + stage * STAGE_DQ;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            copy_rows(kb, row_bytes, key0, p.nk, wave + 4 * i, coff, sb, lane);
-            copy_rows(vb, row_bytes, key0, p.nk, wave + 4 * i, coff, sb + TB, lane);
+            copy_rows(kb, row_bytes, key0, G.nk, wave + 4 * i, coff, sb, lane);
+            copy_rows(vb, row_bytes, key0, G.nk, wave + 4 * i, coff, sb + TB, lane);
         }
     };
     if (ntiles > 0) {
@@ -259,7 +282,7 @@ attn_bwd_dq(BwdParams p) {
             __builtin_amdgcn_sched_barrier(0);
             const int key0 = t * TR;
             // tile entirely visible to the wave's rows: no mask
-            const bool full = key0 + TR <= p.nk && (!p.causal || key0 + TR - 1 <= wrow0);
+            const bool full = key0 + TR <= G.nk && (!G.causal || key0 + TR - 1 <= wrow0);
             bf16x8 dsb[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
@@ -270,7 +293,7 @@ attn_bwd_dq(BwdParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int key = key0 + 16 * kc + 8 * hi + e;
-                        const bool vis = key < p.nk && (!p.causal || key <= qrow);
+                        const bool vis = key < G.nk && (!G.causal || key <= qrow);
                         x[e] = vis ? x[e] : -INFINITY;
                     }
                 }
@@ -294,7 +317,7 @@ attn_bwd_dq(BwdParams p) {
     wait_vmcnt<0>();
 
     // dq[row] += scale * dQ: lane holds head dims dt*32 + 8*i + 4*hi + j
-    if (qrow < p.nq) {
+    if (qrow < G.nq) {
         float *dst = p.dq + qoff + 4 * hi;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
@@ -342,7 +365,10 @@ attn_bwd_dkdv(BwdParams p) {
     // longest (causal: first) key blocks are dispatched first
     int item = blockIdx.x;
     const int inner = p.head_splits * p.hkv * p.b;
-    const int kt = item / inner;
+    const int kt_all = item / inner;
+    const int smp = seq_of(p.tab.tile0, p.tab.nseq, kt_all);
+    const Geo G = geo_of(p, smp);
+    const int kt = kt_all - p.tab.tile0[smp];
     item %= inner;
     const int hs = item % p.head_splits;
     item /= p.head_splits;
@@ -359,8 +385,8 @@ attn_bwd_dkdv(BwdParams p) {
 
     // this lane's key: K (P waves) or V (dS waves) as B operands
     const int key = wkey0 + l32;
-    const int kr = min(key, p.nk - 1);
-    const int64_t koff = ((n * p.two_c + kr) * (int64_t)p.hkv + g) * D;
+    const int kr = min(key, G.nk - 1);
+    const int64_t koff = ((n * p.two_c + G.kv0 + kr) * (int64_t)p.hkv + g) * D;
     bf16x8 bf[D / 16];
     load_b_rows((ds_wave ? p.v : p.k) + koff, hi, bf);
     settle(bf);
@@ -372,13 +398,17 @@ attn_bwd_dkdv(BwdParams p) {
 
     // query tiles: rows from the first one that can see this workgroup's
     // keys (causal: row >= key) to the end, for each of the hpw heads
-    const int qstart = p.causal ? (k0 / TR) : 0;
-    const int nqt = (p.nq + TR - 1) / TR;
+    const int qstart = G.causal ? (k0 / TR) : 0;
+    const int nqt = (G.nq + TR - 1) / TR;
     const int per_head = max(nqt - qstart, 0);
     const int ntiles = per_head * hpw;
     const int64_t row_bytes = (int64_t)p.hq * D * 2;
     const unsigned coff = copy_offset(lane, wave, row_bytes);
-    const int64_t qrow_base = (int64_t)n * p.two_c + p.q_row0;   // global row of local row 0
+    const int64_t qrow_base = (int64_t)n * p.two_c + G.qrow0;   // row of the sample's query 0
+    // lanes 0-31 copy L, lanes 32-63 D; the per-lane base is settled here so
+    // no wait for its load is left inside the tile loop
+    const float *ld_base = hi ? p.delta : p.lse;
+    settle(ld_base);
     // tiles past the last repeat it, so every wave issues 3 copies per tile
     auto issue = [&](int u, int stage) {
         u = min(u, ntiles - 1);
@@ -386,11 +416,11 @@ attn_bwd_dkdv(BwdParams p) {
         const int row0 = (qstart + u % per_head) * TR;
         const unsigned sb = lbase + stage * STAGE_DKDV;
         const int64_t e0 = qrow_base * p.hq * D + (int64_t)head * D;
-        copy_rows(p.q + e0, row_bytes, row0, p.nq, wave, coff, sb, lane);
-        copy_rows(p.dout + e0, row_bytes, row0, p.nq, wave, coff, sb + TB, lane);
-        const int lr = min(row0 + l32, p.nq - 1);
-        const int64_t li = ((int64_t)n * p.hq + head) * p.two_c + p.q_row0 + lr;
-        dma4((hi ? p.delta : p.lse) + li, sb + 2 * TB + wave * LD_SLOT);
+        copy_rows(p.q + e0, row_bytes, row0, G.nq, wave, coff, sb, lane);
+        copy_rows(p.dout + e0, row_bytes, row0, G.nq, wave, coff, sb + TB, lane);
+        const int lr = min(row0 + l32, G.nq - 1);
+        const int64_t li = ((int64_t)n * p.hq + head) * p.two_c + G.qrow0 + lr;
+        dma4(ld_base + li, sb + 2 * TB + wave * LD_SLOT);
     };
     if (ntiles > 0) {
 #pragma unroll
@@ -408,7 +438,7 @@ attn_bwd_dkdv(BwdParams p) {
         issue(it + PDK, ns);
         const int u = ds_wave ? it - 1 : it;
         const int q0 = (qstart + (u < 0 ? 0 : u) % per_head) * TR;
-        if (u >= 0 && u < ntiles && (!p.causal || q0 + TR - 1 >= wkey0)) {
+        if (u >= 0 && u < ntiles && (!G.causal || q0 + TR - 1 >= wkey0)) {
             const unsigned sT = lbase + (ds_wave ? st_ds : st_p) * STAGE_DKDV;
             const unsigned lslot = sT + 2 * TB + wave * LD_SLOT;
             const unsigned slab = slab0 + (u & 1) * (KW * PSLAB);
@@ -430,8 +460,8 @@ attn_bwd_dkdv(BwdParams p) {
             __builtin_amdgcn_sched_barrier(0);
             bf16x8 ob[2];
             if (!ds_wave) {
-                const bool full = q0 + TR <= p.nq && wkey0 + TR <= p.nk &&
-                                  (!p.causal || wkey0 + TR - 1 <= q0);
+                const bool full = q0 + TR <= G.nq && wkey0 + TR <= G.nk &&
+                                  (!G.causal || wkey0 + TR - 1 <= q0);
                 f32x16 x;
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc) {
@@ -445,7 +475,7 @@ attn_bwd_dkdv(BwdParams p) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int row = q0 + 16 * (i >> 3) + 8 * hi + (i & 7);
-                        const bool vis = row < p.nq && key < p.nk && (!p.causal || key <= row);
+                        const bool vis = row < G.nq && key < G.nk && (!G.causal || key <= row);
                         x[i] = vis ? x[i] : -INFINITY;
                     }
                 }
@@ -498,7 +528,7 @@ attn_bwd_dkdv(BwdParams p) {
 
     // dv += dV (P waves), dk += scale dK (dS waves); lane holds head dims
     // dt*32 + 8*i + 4*hi + j.  Split heads add with atomics.
-    if (key < p.nk && ntiles > 0) {
+    if (key < G.nk && ntiles > 0) {
         float *dst = (ds_wave ? p.dk : p.dv) + koff + 4 * hi;
         const float f = ds_wave ? p.scale : 1.0f;
         if (p.head_splits == 1) {
@@ -575,9 +605,10 @@ hipError_t launch_fill_zero(float *x, int64_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_step_bwd_bf16(const StepGeom &g, const void *q, const void *k, const void *v,
-                                const void *dout, const float *lse, const float *delta,
-                                float *dq, float *dk, float *dv, hipStream_t stream) {
+hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode,
+                                const void *q, const void *k, const void *v, const void *dout,
+                                const float *lse, const float *delta, float *dq, float *dk,
+                                float *dv, hipStream_t stream) {
     BwdParams p = {};
     p.q = (const uint16_t *)q;
     p.k = (const uint16_t *)k;
@@ -589,26 +620,34 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const void *q, const void *k,
     p.dk = dk;
     p.dv = dv;
     p.two_c = g.two_c;
-    p.q_row0 = g.q_row0;
-    p.nq = (int)g.nq;
-    p.nk = (int)g.nk;
     p.hq = g.hq;
     p.hkv = g.hkv;
     p.b = (int)g.b;
     p.group = g.hq / g.hkv;
     p.scale = g.scale;
     p.scale_log2 = g.scale_log2;
-    p.causal = g.causal ? 1 : 0;
-    const int rows_wg = TR * NWB;
-    p.ntiles_wg = (int)((g.nq + rows_wg - 1) / rows_wg);
-    hipLaunchKernelGGL(attn_bwd_dq, dim3((unsigned)((int64_t)p.ntiles_wg * g.hq * g.b)),
-                       dim3(64 * NWB), 0, stream, p);
+    p.mode = mode;
+    p.tab = tab;
+    // each sample's query rows (dq: tiles of TR * NWB rows) and keys (dK/dV:
+    // tiles of TR * KW keys) in this mode
+    auto fill_tiles = [&](bool keys, int per_tile) {
+        p.tab.tile0[0] = 0;
+        for (int i = 0; i < tab.nseq; ++i) {
+            const int c = (tab.lcu[i + 1] - tab.lcu[i]) / 2;
+            const int n = keys ? (mode == CPATTN_KV_FIRST_HALF ? c : 2 * c)
+                               : (mode == CPATTN_Q_SECOND_HALF ? c : 2 * c);
+            p.tab.tile0[i + 1] = p.tab.tile0[i] + (n + per_tile - 1) / per_tile;
+        }
+        return (int64_t)p.tab.tile0[tab.nseq];
+    };
+    const int64_t nqt = fill_tiles(false, TR * NWB);
+    hipLaunchKernelGGL(attn_bwd_dq, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * NWB), 0,
+                       stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // key tiles of TR * KW keys; the group's heads split so the grid has
-    // at least ~2 workgroups per CU (heads per workgroup divides the group)
-    p.ntiles_wg = (int)((g.nk + TR * KW - 1) / (TR * KW));
-    const int64_t base_wgs = (int64_t)p.ntiles_wg * g.hkv * g.b;
+    // the group's heads split so the grid has at least ~2 workgroups per CU
+    // (heads per workgroup divides the group)
+    const int64_t base_wgs = fill_tiles(true, TR * KW) * g.hkv * g.b;
     p.head_splits = 1;
     while (p.head_splits < p.group && p.group % (p.head_splits * 2) == 0 &&
            base_wgs * p.head_splits < 512)

@@ -69,11 +69,13 @@ hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
                              const void *vz, void *o, bool out_bf16, float *lse,
                              hipStream_t stream);
 
-// Backward of one step (bf16, d = 128): dq += , dk += , dv += (fp32).
-hipError_t launch_step_bwd_bf16(const StepGeom &g, const void *q, const void *k,
-                                const void *v, const void *dout, const float *lse,
-                                const float *delta, float *dq, float *dk, float *dv,
-                                hipStream_t stream);
+// Backward of one step (bf16, d = 128) for every packed sample of 'tab' in
+// step mode 'mode': dq += , dk += , dv += (fp32).  g supplies b, two_c (the
+// local rows), the heads and the scale.
+hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode,
+                                const void *q, const void *k, const void *v, const void *dout,
+                                const float *lse, const float *delta, float *dq, float *dk,
+                                float *dv, hipStream_t stream);
 
 // delta[n, h, i] = sum_t dout[n, i, h, t] o[n, i, h, t]; o fp32, dout bf16.
 hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o,

@@ -150,6 +150,12 @@ class CPProblem:
 
     def backward(self, grads, o_r, lse_r, do_r, stream=None, scale=0.0):
         """The rank's backward share through cpattn_backward."""
+        if self.cu is not None:
+            C.cpattn_backward_varlen(self.dims, self.dtype, scale, grads["rank"], self.cu,
+                                     self.qz, self.kz, self.vz, o_r, do_r, lse_r,
+                                     grads["delta"], grads["dq"], grads["dkz"], grads["dvz"],
+                                     stream)
+            return
         C.cpattn_backward(self.dims, self.dtype, scale, grads["rank"], self.qz, self.kz,
                           self.vz, o_r, do_r, lse_r, grads["delta"], grads["dq"], grads["dkz"],
                           grads["dvz"], stream)

@@ -259,3 +259,26 @@ def test_varlen_device_calls_validate_before_launch():
     args[3] = 4                                               # rank out of range
     assert L.cpattn_forward_fused_varlen(*args) == C.CPATTN_EINVAL
     del keep, keep2
+
+
+def test_backward_varlen_validates_before_launch():
+    L = C.lib()
+    d = _dims(b=1, s=4096, hq=8, hkv=2, d=128, cp=4)
+    bad, keep = C.make_varlen([0, 100, 4096])
+    good, keep2 = C.make_varlen([0, 1024, 4096])
+    args = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), 1, ctypes.byref(bad)] + \
+        [ALIGNED] * 10 + [0]
+    assert L.cpattn_backward_varlen(*args) == C.CPATTN_ESHAPE
+    args[4] = ctypes.byref(good)
+    args[3] = 4                                               # rank out of range
+    assert L.cpattn_backward_varlen(*args) == C.CPATTN_EINVAL
+    args[3] = 1
+    args[2] = ctypes.c_float(float("nan"))
+    assert L.cpattn_backward_varlen(*args) == C.CPATTN_EINVAL
+    args[2] = ctypes.c_float(0.0)
+    args[1] = C.CPATTN_F32
+    assert L.cpattn_backward_varlen(*args) == C.CPATTN_EDTYPE
+    args[1] = C.CPATTN_BF16
+    args[5] = ALIGNED + 8
+    assert L.cpattn_backward_varlen(*args) == C.CPATTN_EALIGN
+    del keep, keep2

@@ -162,3 +162,90 @@ def test_fused_varlen_full_size_sampled_rows():
         o_ref, l_ref = attention_rows(qf, kf, vf, g - s0 + 1)
         assert_close(f"sample {i} O", o[:, pick], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
         assert_close(f"sample {i} L", l[:, :, pick], l_ref, 1e-3)
+
+
+# --- backward of packed samples ---------------------------------------------
+
+from long_context_causal_amd.inputs import f32_to_bf16_bits  # noqa: E402
+from long_context_causal_amd.runner import to_device  # noqa: E402
+
+GRAD_MAX_REL, GRAD_MEAN_REL = 1e-2, 5e-3      # as the unpacked backward (test_gpu_backward)
+
+
+def _assert_grad(name, got, ref):
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    mx, mn = err.max(), err.mean()
+    rmx, rmn = np.abs(ref).max(), np.abs(ref).mean()
+    say(f"  [{name}] max_err={mx:.3e} ({mx / rmx:.2e} of max|ref|) "
+        f"mean_err={mn:.3e} ({mn / rmn:.2e} of mean|ref|)")
+    assert mx <= GRAD_MAX_REL * rmx and mn <= GRAD_MEAN_REL * rmn
+
+
+BWD = [("bf16_gqa_s8k_cp4", [100, 1, 37, 64]),
+       ("bf16_gqa_s32k_cp8", [40, 130, 3]),
+       ("bf16_mha_s16k_cp4_widelogits", [96, 5, 64]),
+       ("bf16_gqa_s128k_cp16_rope", [24, 7, 9])]
+
+
+@pytest.mark.parametrize("name,chunks", BWD)
+def test_backward_varlen_all_ranks(name, chunks):
+    base = WORKLOADS[name]
+    cu = _cu(base.cp, chunks)
+    w = small(base, int(cu[-1]))
+    say(f"backward varlen {name} cu={cu.tolist()}")
+    q, k, v = make_inputs(w)
+    rng = np.random.default_rng(99)
+    do = f32_to_bf16_bits(rng.standard_normal((w.b, w.s, w.hq, w.d)).astype(np.float32))
+    P = CPProblem(w, q, k, v, cu_seqlens=cu)
+    P.partition()
+    doz = ovl.partition(as_f32(do), cu, w.cp)
+    tloc = w.s // w.cp
+    dq_z = np.zeros((w.cp, w.b, tloc, w.hq, w.d))
+    dk_z = np.zeros((w.cp, w.b, tloc, w.hkv, w.d))
+    dv_z = np.zeros_like(dk_z)
+    for r in range(w.cp):
+        out = P.alloc_out(r, C.CPATTN_F32)
+        P.forward_fused(out)
+        g = P.alloc_grads(r)
+        P.backward(g, out["o"], out["lse"],
+                   to_device(f32_to_bf16_bits(doz[r].astype(np.float32))))
+        torch.cuda.synchronize()
+        dq_z[r] = g["dq"].cpu().numpy()
+        dk_z += g["dkz"].cpu().numpy()        # the reduce-scatter, summed on the owner
+        dv_z += g["dvz"].cpu().numpy()
+    qf, kf = as_f32(q).astype(np.float64), as_f32(k).astype(np.float64)
+    if w.rope_theta is not None:           # gradients are taken at the rotated Q, K
+        pos = ovl.sample_positions(cu)
+        qf, kf = ocp.rope(qf, pos, w.rope_theta), ocp.rope(kf, pos, w.rope_theta)
+    dq, dk, dv = ovl.packed_causal_attention_bwd(qf, kf, as_f32(v).astype(np.float64),
+                                                 as_f32(do).astype(np.float64), cu)
+    _assert_grad("dQ", ovl.unpartition(dq_z, cu), dq)
+    _assert_grad("dK", ovl.unpartition(dk_z, cu), dk)
+    _assert_grad("dV", ovl.unpartition(dv_z, cu), dv)
+
+
+def test_backward_varlen_one_sample_is_unpacked():
+    w = small(WORKLOADS["bf16_gqa_s32k_cp8"], 2 * 8 * 136)
+    say("backward varlen, one sample")
+    q, k, v = make_inputs(w)
+    rng = np.random.default_rng(5)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    Pv = CPProblem(w, q, k, v, cu_seqlens=[0, w.s])
+    Pv.partition()
+    r = w.rank
+    out = P.alloc_out(r, C.CPATTN_F32)
+    P.forward_fused(out)
+    do_r = to_device(f32_to_bf16_bits(
+        rng.standard_normal(tuple(out["o"].shape)).astype(np.float32)))
+    g, gv = P.alloc_grads(r), Pv.alloc_grads(r)
+    P.backward(g, out["o"], out["lse"], do_r)
+    Pv.backward(gv, out["o"], out["lse"], do_r)
+    torch.cuda.synchronize()
+    # dq is written by one workgroup per row; dK/dV add with atomics whose
+    # order may differ, so they agree to fp32 rounding
+    assert torch.equal(g["dq"], gv["dq"])
+    for key in ("dkz", "dvz"):
+        np.testing.assert_allclose(gv[key].cpu().numpy(), g[key].cpu().numpy(), rtol=1e-5,
+                                   atol=1e-6)

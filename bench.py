@@ -256,10 +256,28 @@ def main():
         # pairs per (batch, head) with c the sample's chunk length
         v_flops = sum(dataclasses.replace(w, s=int(cu[i + 1] - cu[i])).rank_flops()
                       for i in range(len(cu) - 1))
+        # the packed share's backward (seeded bf16 dO, its own O and L)
+        gen_v = torch.Generator(device="cuda")
+        gen_v.manual_seed(98)
+        do_v = torch.randn(vout["o"].shape, generator=gen_v, device="cuda").to(torch.bfloat16)
+        gv = Pv.alloc_grads(rank)
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                Pv.backward(gv, vout["o"], vout["lse"], do_v, stream)
+            torch.cuda.synchronize()
+            vb_ev = []
+            for _ in range(args.steps):
+                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record(stream)
+                Pv.backward(gv, vout["o"], vout["lse"], do_v, stream)
+                e1.record(stream)
+                vb_ev.append((e0, e1))
+            torch.cuda.synchronize()
         varlen = {"cu": cu, "flops": v_flops,
                   "ms": float(np.mean([a.elapsed_time(b) for a, b in v_total])),
-                  "attn_ms": float(np.mean([a.elapsed_time(b) for a, b in v_attn]))}
-        del Pv, vout
+                  "attn_ms": float(np.mean([a.elapsed_time(b) for a, b in v_attn])),
+                  "bwd_ms": float(np.mean([a.elapsed_time(b) for a, b in vb_ev]))}
+        del Pv, vout, gv, do_v
 
     # the backward of the same share: dO seeded bf16, the rank's merged O
     # and L from the forward above
@@ -366,6 +384,8 @@ def main():
             "avg_launch_ms": round(varlen["attn_ms"], 4),
             "achieved": round(v_tf, 2),
             "frac": round(v_tf / peak, 4),
+            "backward_ms": round(varlen["bwd_ms"], 4),
+            "backward_value": round(2.5 * varlen["flops"] / (varlen["bwd_ms"] * 1e-3) / 1e12, 2),
         }
     if backward is not None:
         b_flops = 2.5 * flops

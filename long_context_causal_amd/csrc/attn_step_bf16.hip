@@ -331,7 +331,7 @@ struct Kernel {
         const bool mask = (tr.key0 + BN > tr.nk) || (tr.causal && tr.key0 + BN - 1 > wrow0) ||
                           wrow0 < tr.min_row;
         float tmax = mask ? tile_max<true>(tr, S, qrow, hi) : tile_max<false>(tr, S, qrow, hi);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * p.scale_log2;
+        tmax = halves_max(tmax) * p.scale_log2;
         const float m_new = fmaxf(S.m_run, tmax);
         if (__builtin_amdgcn_ballot_w64(m_new > S.m_run + RESCALE_SLACK)) {
             // a row that has seen no visible key yet (m = -inf) keeps alpha 1
@@ -511,7 +511,7 @@ struct Kernel {
 
         // Normalise and store O (fp32, or bf16 rounded to nearest even) and
         // L (natural log).
-        const float lt = S.l_run + __shfl_xor(S.l_run, 32);
+        const float lt = halves_sum(S.l_run);
         const int row = wrow0 + l32;
         if (row < P.nq) {
             const float inv = 1.0f / lt;

@@ -51,6 +51,27 @@ __device__ __forceinline__ bf16x8 vt_read(unsigned addr) {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Reductions across the two 32-lane halves of a wave (lane l with l ^ 32)
+// by one v_permlane32_swap: it exchanges the upper half of its first operand
+// with the lower half of its second, so with x in both every lane ends up
+// holding {x[l], x[l ^ 32]} in the pair, in some order.  A plain VALU
+// instruction: unlike a lane shuffle it does not go through the LDS queue.
+__device__ __forceinline__ void swap_halves(float &a, float &b) {
+    // two wait states on each side cover the VALU-write and result-read
+    // hazards that the compiler does not see through inline asm
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float halves_max(float x) {
+    float y = x;
+    swap_halves(x, y);
+    return fmaxf(x, y);
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    float y = x;
+    swap_halves(x, y);
+    return x + y;
+}
+
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>

@@ -3,9 +3,12 @@
 A step is one pass of the whole path over one batch of synthetic input
 already resident in HBM: the zigzag split of Q, K and V (three
 cpattn_partition launches), the cp blockwise-attention steps of the
-measured rank (cpattn_step_fwd; at step i the rank reads the K/V block of
-rank (rank - i) mod cp) and the LSE merge (cpattn_merge).  W untimed
-warm-up steps, then K timed steps bracketed by synchronisation.
+measured rank (at step i the rank reads the K/V block of rank (rank - i)
+mod cp; all cp steps as one grid through cpattn_forward_steps, each step
+writing its own partial O_i and L_i) and the LSE merge (cpattn_merge).  W
+untimed warm-up steps, then K timed steps bracketed by synchronisation.
+The same steps launched one by one (cpattn_step_fwd) are reported under
+"per_step_launches".
 
 The same share is also timed through the fused form (the split, then one
 cpattn_forward_fused launch that carries the online softmax across the cp
@@ -75,7 +78,7 @@ def committed_traffic(workload, key="attention_traffic_bytes_per_launch"):
     figure no longer describes this kernel and None is returned.
     """
     import hashlib
-    prof = os.path.join(ROOT, "profiles", f"attn_step_bf16__{workload}__hbm_traffic.txt")
+    prof = os.path.join(ROOT, "profiles", f"attn_steps_bf16__{workload}__hbm_traffic.txt")
     if not os.path.exists(prof):
         return None
     h = hashlib.sha256()
@@ -129,22 +132,20 @@ def cpu_baseline(w, q, k, v, rank, target_s):
 
 
 def share_step_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
-    """(attention TFLOP/s over the summed step-kernel times, TFLOP/s over
-    steps + merge) of one rank's share, from HIP events on ``stream``."""
+    """(attention TFLOP/s of the steps' grid, TFLOP/s over steps + merge) of
+    one rank's share, from HIP events on ``stream``."""
     import numpy as np
     buf = P.alloc_rank(rank, C.CPATTN_F32)
     with torch.cuda.stream(stream):
         for _ in range(warmup):
-            for i in range(w.cp):
-                P.step(buf, i, stream)
+            P.steps(buf, stream)
             P.merge(buf, stream)
         torch.cuda.synchronize()
         ev = []
         for _ in range(reps):
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             e[0].record(stream)
-            for i in range(w.cp):
-                P.step(buf, i, stream)
+            P.steps(buf, stream)
             e[1].record(stream)
             P.merge(buf, stream)
             e[2].record(stream)
@@ -187,9 +188,8 @@ def main():
         mark("start")
         P.partition(stream)
         mark("partition")
-        for i in range(w.cp):
-            P.step(buf, i, stream)
-            mark(f"step{i}")
+        P.steps(buf, stream)
+        mark("steps")
         P.merge(buf, stream)
         mark("merge")
 
@@ -205,6 +205,25 @@ def main():
             all_evs.append(evs)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+
+    # the same steps launched one by one (cpattn_step_fwd), each timed
+    per_step = None
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            for i in range(w.cp):
+                P.step(buf, i, stream)
+        torch.cuda.synchronize()
+        ps_ev = []
+        for _ in range(args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(w.cp + 1)]
+            e[0].record(stream)
+            for i in range(w.cp):
+                P.step(buf, i, stream)
+                e[i + 1].record(stream)
+            ps_ev.append(e)
+        torch.cuda.synchronize()
+    per_step = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ps_ev]))
+                for i in range(w.cp)]
 
     # the fused form of the same share: split, then one launch
     fused = None
@@ -302,21 +321,16 @@ def main():
         backward = float(np.mean([a.elapsed_time(b) for a, b in b_ev]))
 
     # per-kernel times (ms) from the events, averaged over the timed steps
-    part_ms, merge_ms, step_ms, total_ms = [], [], [[] for _ in range(w.cp)], []
+    part_ms, merge_ms, grid_ms, total_ms = [], [], [], []
     for evs in all_evs:
         d = dict(evs)
-        names = [t for t, _ in evs]
         part_ms.append(d["start"].elapsed_time(d["partition"]))
-        prev = "partition"
-        for i in range(w.cp):
-            step_ms[i].append(d[prev].elapsed_time(d[f"step{i}"]))
-            prev = f"step{i}"
-        merge_ms.append(d[prev].elapsed_time(d["merge"]))
-        total_ms.append(d["start"].elapsed_time(d[names[-1]]))
+        grid_ms.append(d["partition"].elapsed_time(d["steps"]))
+        merge_ms.append(d["steps"].elapsed_time(d["merge"]))
+        total_ms.append(d["start"].elapsed_time(d["merge"]))
     mean = lambda xs: float(np.mean(xs))
     ms_step = mean(total_ms)
-    steps_ms = [mean(x) for x in step_ms]
-    attn_ms = sum(steps_ms)
+    attn_ms = mean(grid_ms)
     flops = w.rank_flops()
     value = flops / (ms_step * 1e-3) / 1e12
 
@@ -346,13 +360,20 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": committed_traffic(w.name) if w.dtype == "bf16" else None,
-                     "kernel": "attn_step_bf16" if w.dtype == "bf16" else "attn_step_f32",
-                     "flops_per_launch": flops / w.cp,
-                     "avg_launch_ms": round(attn_ms / w.cp, 4)},
+                     "kernel": "attn_steps_bf16" if w.dtype == "bf16" else "attn_step_f32",
+                     "flops_per_launch": flops if w.dtype == "bf16" else flops / w.cp,
+                     "avg_launch_ms": round(attn_ms if w.dtype == "bf16" else attn_ms / w.cp,
+                                            4)},
         "pct_of_peak": round(100 * value / peak, 2),
         "kernels_ms": {"partition_qkv": round(mean(part_ms), 4),
-                       "steps": [round(x, 4) for x in steps_ms],
+                       "steps": round(attn_ms, 4),
                        "merge": round(mean(merge_ms), 4)},
+        "per_step_launches": {"entry_point": "cpattn_step_fwd",
+                              "kernel": "attn_step_bf16" if w.dtype == "bf16"
+                              else "attn_step_f32",
+                              "ms": [round(x, 4) for x in per_step],
+                              "attention_tflops": round(flops / (sum(per_step) * 1e-3) / 1e12,
+                                                        2)},
         "attention_tflops": round(attn_tflops, 2),
         "steps_plus_merge_tflops": round(flops / ((attn_ms + mean(merge_ms)) * 1e-3) / 1e12, 2),
         "partition_gbps": round(part_bytes / (mean(part_ms) * 1e-3) / 1e9, 1),

@@ -176,6 +176,22 @@ int cpattn_merge(const cpattn_dims *dims, int n, const cpattn_partial *p,
  * partials of all cp steps).  Returns 0 on invalid dims or rank. */
 size_t cpattn_forward_workspace(const cpattn_dims *dims, int rank);
 
+/* The cp steps of one rank's forward share ("Megatron-LM 篇" 3.2 step 2,
+ * the steps of cpattn_step_mode), device, without the merge: step i reads
+ * the source rank's K/V block of the partitioned qz/kz/vz ([cp, b, 2c, h, d]
+ * as written by cpattn_partition) and writes its partial O_i and L_i, exactly
+ * as cpattn_step_fwd would, into the workspace ws in step order: for each
+ * step its O ([b, rows_i, hq, d] fp32), then its L ([b, hq, rows_i] fp32),
+ * each starting on a 256-byte boundary (rows_i as for cpattn_step_fwd).
+ * CPATTN_BF16 runs all steps as one grid (the steps are independent, so
+ * their workgroups overlap one another's loads and stores); CPATTN_F32
+ * launches them one by one.  ws: at least cpattn_forward_workspace bytes
+ * (ENOSPACE otherwise), 256-byte aligned (EALIGN).  The partials stay in ws
+ * for cpattn_merge. */
+int cpattn_forward_steps(const cpattn_dims *dims, int dtype, float scale, int rank,
+                         const void *qz, const void *kz, const void *vz, void *ws,
+                         size_t ws_bytes, void *stream);
+
 /* One rank's whole forward share, device: the cp steps of
  * cpattn_step_mode, each reading the source rank's K/V block of the
  * partitioned qz/kz/vz ([cp, b, 2c, h, d] as written by cpattn_partition),

@@ -81,6 +81,8 @@ def lib():
         L.cpattn_merge.argtypes = [D, I, ctypes.POINTER(cpattn_partial), I, P, P, P]
         L.cpattn_forward_workspace.argtypes = [D, I]
         L.cpattn_forward_workspace.restype = ctypes.c_size_t
+        L.cpattn_forward_steps.argtypes = [D, I, ctypes.c_float, I, P, P, P, P,
+                                           ctypes.c_size_t, P]
         L.cpattn_forward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, ctypes.c_size_t,
                                      I, P, P, P]
         L.cpattn_forward_fused.argtypes = [D, I, ctypes.c_float, I, P, P, P, I, P, P, P]
@@ -98,7 +100,7 @@ def lib():
         L.cpattn_status_str.argtypes = [I]
         L.cpattn_status_str.restype = ctypes.c_char_p
         for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
-                     "cpattn_step_fwd", "cpattn_merge", "cpattn_forward",
+                     "cpattn_step_fwd", "cpattn_merge", "cpattn_forward_steps", "cpattn_forward",
                      "cpattn_forward_fused", "cpattn_bwd_delta", "cpattn_step_bwd",
                      "cpattn_backward", "cpattn_partition_positions_varlen",
                      "cpattn_partition_varlen", "cpattn_forward_fused_varlen",
@@ -178,6 +180,13 @@ def cpattn_merge(dims, partials, out_dtype, o_out, lse_out=None, stream=None):
 
 def cpattn_forward_workspace(dims, rank):
     return int(lib().cpattn_forward_workspace(ctypes.byref(dims), rank))
+
+
+def cpattn_forward_steps(dims, dtype, scale, rank, qz, kz, vz, ws, ws_bytes, stream=None):
+    _check(lib().cpattn_forward_steps(ctypes.byref(dims), dtype, float(scale), rank, _ptr(qz),
+                                      _ptr(kz), _ptr(vz), _ptr(ws), int(ws_bytes),
+                                      _stream(stream)),
+           "cpattn_forward_steps")
 
 
 def cpattn_forward(dims, dtype, scale, rank, qz, kz, vz, ws, ws_bytes, out_dtype, o_out,

@@ -91,6 +91,23 @@ size_t partial_l_bytes(const cpattn_dims &d, int64_t rows) {
     return round256((size_t)d.b * d.hq * rows * sizeof(float));
 }
 
+// Device partials of rank's steps, carved from ws in step order (O then L,
+// 256-byte rounded), and the merge descriptors over them.
+void carve_partials(const cpattn_dims &d, int rank, void *ws, cpattn_partial *parts) {
+    char *cursor = (char *)ws;
+    const int64_t two_c = d.s / d.cp;
+    for (int i = 0; i < d.cp; ++i) {
+        int mode, src;
+        cpattn_step_mode(i, rank, d.cp, &mode, &src);
+        const int64_t rows = step_rows(d, mode);
+        parts[i].o = (float *)cursor;
+        cursor += partial_o_bytes(d, rows);
+        parts[i].lse = (float *)cursor;
+        cursor += partial_l_bytes(d, rows);
+        parts[i].row0 = mode == CPATTN_Q_SECOND_HALF ? two_c / 2 : 0;
+        parts[i].rows = rows;
+    }
+}
 }  // namespace
 
 extern "C" {
@@ -237,50 +254,68 @@ size_t cpattn_forward_workspace(const cpattn_dims *dims, int rank) {
     return total;
 }
 
-int cpattn_forward(const cpattn_dims *dims, int dtype, float scale, int rank, const void *qz,
-                   const void *kz, const void *vz, void *ws, size_t ws_bytes, int out_dtype,
-                   void *o_out, float *lse_out, void *stream) {
+
+int cpattn_forward_steps(const cpattn_dims *dims, int dtype, float scale, int rank,
+                         const void *qz, const void *kz, const void *vz, void *ws,
+                         size_t ws_bytes, void *stream) {
     int st = check_dims(dims);
     if (st) return st;
     if (rank < 0 || rank >= dims->cp) return CPATTN_EINVAL;
-    if (!qz || !kz || !vz || !ws || !o_out) return CPATTN_EINVAL;
+    if (!qz || !kz || !vz || !ws) return CPATTN_EINVAL;
     if (((uintptr_t)ws & 255u) != 0) return CPATTN_EALIGN;
     if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return CPATTN_EDTYPE;
-    if (out_dtype != CPATTN_F32 && out_dtype != CPATTN_BF16) return CPATTN_EDTYPE;
     if (dtype == CPATTN_BF16 && dims->d != 128) return CPATTN_ESHAPE;
-    if ((int64_t)dims->hq * dims->cp > CPATTN_MAX_MERGE_WEIGHTS) return CPATTN_ESHAPE;
-    if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz) || !aligned16(o_out) ||
-        (lse_out && ((uintptr_t)lse_out & 3u)))
-        return CPATTN_EALIGN;
-    const size_t need = cpattn_forward_workspace(dims, rank);
-    if (ws_bytes < need) return CPATTN_ENOSPACE;
+    if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz)) return CPATTN_EALIGN;
+    if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
+    if (ws_bytes < cpattn_forward_workspace(dims, rank)) return CPATTN_ENOSPACE;
 
     const size_t es = dtype == CPATTN_BF16 ? 2 : 4;
     const int64_t two_c = dims->s / dims->cp;
     const size_t q_block = (size_t)dims->b * two_c * dims->hq * dims->d * es;
     const size_t kv_block = (size_t)dims->b * two_c * dims->hkv * dims->d * es;
     const char *q_r = (const char *)qz + rank * q_block;
-
     cpattn_partial parts[CPATTN_MAX_PARTIALS];
-    char *cursor = (char *)ws;
+    carve_partials(*dims, rank, ws, parts);
+    StepGeom geo[CPATTN_MAX_PARTIALS];
+    const void *ks[CPATTN_MAX_PARTIALS], *vs[CPATTN_MAX_PARTIALS];
+    float *os[CPATTN_MAX_PARTIALS], *ls[CPATTN_MAX_PARTIALS];
     for (int i = 0; i < dims->cp; ++i) {
         int mode, src;
         cpattn_step_mode(i, rank, dims->cp, &mode, &src);
-        const int64_t rows = step_rows(*dims, mode);
-        float *o = (float *)cursor;
-        cursor += partial_o_bytes(*dims, rows);
-        float *lse = (float *)cursor;
-        cursor += partial_l_bytes(*dims, rows);
         // ring hand-off: step i reads rank src's partitioned K/V block
-        const char *k_src = (const char *)kz + src * kv_block;
-        const char *v_src = (const char *)vz + src * kv_block;
-        st = cpattn_step_fwd(dims, dtype, scale, mode, q_r, k_src, v_src, o, lse, stream);
-        if (st) return st;
-        parts[i].o = o;
-        parts[i].lse = lse;
-        parts[i].row0 = mode == CPATTN_Q_SECOND_HALF ? two_c / 2 : 0;
-        parts[i].rows = rows;
+        ks[i] = (const char *)kz + src * kv_block;
+        vs[i] = (const char *)vz + src * kv_block;
+        os[i] = (float *)parts[i].o;
+        ls[i] = (float *)parts[i].lse;
+        if (dtype == CPATTN_F32) {
+            st = cpattn_step_fwd(dims, dtype, scale, mode, q_r, ks[i], vs[i], os[i], ls[i],
+                                 stream);
+            if (st) return st;
+        }
+        geo[i] = cpattn::step_geom(*dims, mode, scale);
     }
+    if (dtype == CPATTN_F32) return CPATTN_OK;
+    // one grid: 256-row query tiles of every step, all heads and batches
+    if ((two_c + 255) / 256 * dims->hq * dims->b * dims->cp > (int64_t)INT32_MAX)
+        return CPATTN_ESHAPE;
+    return status_of(
+        cpattn::launch_steps_bf16(dims->cp, geo, q_r, ks, vs, os, ls, (hipStream_t)stream));
+}
+
+int cpattn_forward(const cpattn_dims *dims, int dtype, float scale, int rank, const void *qz,
+                   const void *kz, const void *vz, void *ws, size_t ws_bytes, int out_dtype,
+                   void *o_out, float *lse_out, void *stream) {
+    int st = check_dims(dims);
+    if (st) return st;
+    if (rank < 0 || rank >= dims->cp) return CPATTN_EINVAL;
+    if (!o_out) return CPATTN_EINVAL;
+    if (out_dtype != CPATTN_F32 && out_dtype != CPATTN_BF16) return CPATTN_EDTYPE;
+    if ((int64_t)dims->hq * dims->cp > CPATTN_MAX_MERGE_WEIGHTS) return CPATTN_ESHAPE;
+    if (!aligned16(o_out) || (lse_out && ((uintptr_t)lse_out & 3u))) return CPATTN_EALIGN;
+    st = cpattn_forward_steps(dims, dtype, scale, rank, qz, kz, vz, ws, ws_bytes, stream);
+    if (st) return st;
+    cpattn_partial parts[CPATTN_MAX_PARTIALS];
+    carve_partials(*dims, rank, ws, parts);
     return cpattn_merge(dims, dims->cp, parts, out_dtype, o_out, lse_out, stream);
 }
 

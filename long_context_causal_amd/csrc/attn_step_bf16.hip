@@ -206,6 +206,12 @@ struct FusedPlan {
     }
 };
 
+// Workgroup index in the order that gives each XCD a contiguous run (the
+// dispatcher deals workgroups to the 8 XCDs round robin).
+__device__ __forceinline__ int xcd_order(int blk, int nblk) {
+    return (nblk & 7) == 0 ? (blk & 7) * (nblk >> 3) + (blk >> 3) : blk;
+}
+
 template <class Plan, bool OUT_BF16>
 struct Kernel {
     // Per-wave state.
@@ -255,30 +261,53 @@ struct Kernel {
         }
     }
 
+    // LDS operands of matrix step i (see matrix_phase): the two K chunks of
+    // k-step i and the two V^T blocks of head-dim tiles 2(i%2), 2(i%2)+1 of
+    // key chunk i/2.
+    __device__ __forceinline__ static void step_reads(const State &S, int i, bf16x8 (&kf)[2],
+                                                      bf16x8 (&vf)[2]) {
+        kf[0] = k_read(S.koff[i]);
+        kf[1] = k_read(S.koff[i] + 32 * ROWB);
+        const int kc = i >> 1, dt0 = 2 * (i & 1);
+        vf[0] = vt_read(S.voff[dt0] + kc * 16 * ROWB);
+        vf[1] = vt_read(S.voff[dt0 + 1] + kc * 16 * ROWB);
+    }
+
+    // The operands of the first two matrix steps, read ahead: a wave issues
+    // them at the end of its vector half so that their LDS latency passes
+    // while it waits at the barrier, and its matrix phase starts on resident
+    // operands.
+    struct Ahead {
+        bf16x8 kf[2][2], vf[2][2];
+    };
+    __device__ __forceinline__ static void read_ahead(const State &S, Ahead &A) {
+        step_reads(S, 0, A.kf[0], A.vf[0]);
+        step_reads(S, 1, A.kf[1], A.vf[1]);
+    }
+
     // Matrix phase: S^T(t) = K(t) Q^T and O^T += V(t-1)^T P(t-1), from the
-    // stages S.koff / S.voff point at.  One code path for every phase: the
-    // first phase multiplies a zeroed V tile by P = 0, and the S^T of the
-    // phase after a wave's last tile is computed on resident rows and dropped.
-    __device__ __forceinline__ static void matrix_phase(State &S) {
+    // stages S.koff / S.voff point at, its first two steps' operands in A.
+    // One code path for every phase: the first phase multiplies a zeroed V
+    // tile by P = 0, and the S^T of the phase after a wave's last tile is
+    // computed on resident rows and dropped.
+    __device__ __forceinline__ static void matrix_phase(State &S, const Ahead &A) {
         // Eight steps of four MFMAs: step i does k-step i of S^T (both 32-key
         // halves) and head-dim tiles 2(i%2), 2(i%2)+1 of key chunk i/2 of O^T.
         // The LDS reads of step i+2 are issued before the MFMAs of step i, so
         // two steps of matrix work cover each read's latency (the fences keep
         // the compiler from hoisting every read, which would exhaust registers).
         bf16x8 kf[3][2], vf[3][2];
-        auto reads = [&](int i, int slot) {
-            kf[slot][0] = k_read(S.koff[i]);
-            kf[slot][1] = k_read(S.koff[i] + 32 * ROWB);
-            const int kc = i >> 1, dt0 = 2 * (i & 1);
-            vf[slot][0] = vt_read(S.voff[dt0] + kc * 16 * ROWB);
-            vf[slot][1] = vt_read(S.voff[dt0 + 1] + kc * 16 * ROWB);
-        };
-        reads(0, 0);
-        reads(1, 1);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            kf[0][j] = A.kf[0][j];
+            vf[0][j] = A.vf[0][j];
+            kf[1][j] = A.kf[1][j];
+            vf[1][j] = A.vf[1][j];
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int cur = i % 3;
-            if (i + 2 < 8) reads(i + 2, (i + 2) % 3);
+            if (i + 2 < 8) step_reads(S, i + 2, kf[(i + 2) % 3], vf[(i + 2) % 3]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
@@ -363,21 +392,41 @@ struct Kernel {
         S.l_run += lsum0 + lsum1;
     }
 
-    // The barrier opening half-iteration h.  At even h = 2u: this wave's
-    // copies of tile u are complete before it (the copies of tile u+1 may
-    // still fly), and the copies of tile u+2 are issued after it.
+    // The barrier opening half-iteration h.  Before it this wave's copies of
+    // tile (h+1)/2 are complete (only the copies of the tile after may still
+    // fly), so tile u is resident from barrier 2u-1 on; after it, at even
+    // h = 2u, the copies of tile u+2 are issued.  No LDS wait: a matrix phase
+    // consumes its own reads, and the reads a wave issues ahead of the
+    // barrier touch stages that no copy in flight or issued here overwrites.
     __device__ __forceinline__ static void sync(const Plan &P, State &S, int h,
                                                 unsigned lds_addr, int wave) {
         const bool even = (h & 1) == 0;
-        if (even) wait_vmcnt<LPT>();
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        wait_vmcnt<LPT>();
+        asm volatile("s_barrier" ::: "memory");
         if (even) {
             const int u = (h >> 1) + 2;
             issue(S, lds_addr + (u % NS) * 2 * TILEB, P.tile(u), wave);
         }
     }
 
+    // Workgroup -> (batch, kv group, query tile, head in group).  The 8
+    // XCDs receive workgroups round robin; give each a contiguous run of
+    // items so heads sharing a KV group share that XCD's L2.  Causal steps
+    // take their longest query tiles first.
     __device__ __forceinline__ static void run(const Params &p, char *lds) {
+        int item = xcd_order(blockIdx.x, gridDim.x);
+        const int hh = item % p.group;
+        item /= p.group;
+        const int qt_rank = item % p.num_qtiles;
+        item /= p.num_qtiles;
+        const int g = item % p.hkv;
+        const int n = item / p.hkv;
+        run_item(p, lds, n, g, hh, Plan::kLongestFirst ? p.num_qtiles - 1 - qt_rank : qt_rank);
+    }
+
+    // The query tile qt of head g * group + hh of batch element n.
+    __device__ __forceinline__ static void run_item(const Params &p, char *lds, int n, int g,
+                                                    int hh, int qt) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         // wave index as a scalar: every per-wave decision below is a scalar
@@ -386,23 +435,9 @@ struct Kernel {
         const int grp = wave >> 2;                   // 0: leading, 1: trailing group
         const int hi = lane >> 5;
         const int l32 = lane & 31;
-
-        // Workgroup -> (batch, kv group, query tile, head in group).  The 8
-        // XCDs receive workgroups round robin; give each a contiguous run of
-        // items so heads sharing a KV group share that XCD's L2.  Causal
-        // steps take their longest query tiles first.
-        int item = blockIdx.x;
-        const int nblk = gridDim.x;
-        if ((nblk & 7) == 0) item = (item & 7) * (nblk >> 3) + (item >> 3);
-        const int hh = item % p.group;
-        item /= p.group;
-        const int qt_rank = item % p.num_qtiles;
-        item /= p.num_qtiles;
-        const int g = item % p.hkv;
-        const int n = item / p.hkv;
         const int head = g * p.group + hh;
         Plan P;
-        P.init(p, Plan::kLongestFirst ? p.num_qtiles - 1 - qt_rank : qt_rank, n, g);
+        P.init(p, qt, n, g);
         const int wrow0 = P.qtile * BM + wave * 32;   // first row of this wave in its sequence
         const int ntiles = P.ntiles;
         State S;
@@ -476,12 +511,16 @@ struct Kernel {
         // A wave computes tile t when P.comp(t): the matrix phase G(t) runs
         // when it needs S(t) or adds P(t-1); after a tile the wave skips, P is
         // zero, so a following G adds nothing for it.
-        if (grp == 1) sync(P, S, 0, lds_addr, wave);
+        // The zero stage's writes complete before the first barrier.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        sync(P, S, 0, lds_addr, wave);
+        Ahead A;
+        read_ahead(S, A);
+        if (grp == 1) sync(P, S, 1, lds_addr, wave);
         for (int t = 0; t <= ntiles; ++t) {
-            const int hg = 2 * t + grp;
-            sync(P, S, hg, lds_addr, wave);
+            const int hg = 2 * t + grp;    // the barrier this wave last passed
             if (P.comp(t, wrow0) || P.comp(t - 1, wrow0))
-                matrix_phase(S);
+                matrix_phase(S, A);
             if (t == ntiles) break;
             sync(P, S, hg + 1, lds_addr, wave);
             if (P.comp(t, wrow0)) {
@@ -503,6 +542,9 @@ struct Kernel {
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt) S.voff[dt] += vstep;
             }
+            // K(t+1) is resident since barrier 2t+1, V(t) since barrier 2t
+            read_ahead(S, A);
+            sync(P, S, hg + 2, lds_addr, wave);
         }
         if (grp == 0) sync(P, S, 2 * ntiles + 1, lds_addr, wave);
         // copies issued past the end land in stages nobody reads; retire them
@@ -547,6 +589,62 @@ attn_step_bf16(Params p) {
     Kernel<StepPlan<CAUSAL>, false>::run(p, lds);
 }
 
+// Several CP steps of one rank in one launch (fp32 partial outputs).  The
+// steps are independent: step j reads its source block and writes its own
+// partial, exactly as its own launch of attn_step_bf16 would.  One grid
+// lets the workgroup scheduler start a step's query tiles while another
+// step's workgroups are still storing their outputs, where separate
+// launches make every CU load and store at the same moments.
+struct StepDesc {
+    const uint16_t *k, *v;   // the source rank's block
+    float *o, *lse;          // the step's partial
+    int q_row0, nq, nk, causal, num_qtiles;
+    int item0;               // first workgroup of the step within one (batch, KV head)
+};
+constexpr int MAX_STEPS = 32;   // steps per launch (kernel argument space)
+struct StepsParams {
+    const uint16_t *q;
+    int64_t two_c;
+    int hq, hkv, group, nsteps, items;   // items: workgroups per (batch, KV head)
+    float scale_log2;
+    StepDesc st[MAX_STEPS];
+};
+
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_steps_bf16(StepsParams sp) {
+    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
+    // workgroup -> (batch, KV head), then the step, then (query tile, head
+    // in group) inside the step; the steps are laid out longest items first
+    const int item = xcd_order(blockIdx.x, gridDim.x);
+    const int ng = item / sp.items;
+    int w = item - ng * sp.items;
+    int j = 0;
+    while (j + 1 < sp.nsteps && sp.st[j + 1].item0 <= w) ++j;
+    const StepDesc &d = sp.st[j];
+    w -= d.item0;
+    Params p = {};
+    p.q = sp.q;
+    p.k = d.k;
+    p.v = d.v;
+    p.o = d.o;
+    p.lse = d.lse;
+    p.two_c = sp.two_c;
+    p.q_row0 = d.q_row0;
+    p.nq = d.nq;
+    p.nk = d.nk;
+    p.hq = sp.hq;
+    p.hkv = sp.hkv;
+    p.group = sp.group;
+    p.num_qtiles = d.num_qtiles;
+    p.scale_log2 = sp.scale_log2;
+    const int hh = w % sp.group, qt_rank = w / sp.group;
+    const int g = ng % sp.hkv, n = ng / sp.hkv;
+    if (d.causal)
+        Kernel<StepPlan<true>, false>::run_item(p, lds, n, g, hh, d.num_qtiles - 1 - qt_rank);
+    else
+        Kernel<StepPlan<false>, false>::run_item(p, lds, n, g, hh, qt_rank);
+}
+
 // A rank's whole share (merged output, fp32 or bf16).
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -583,6 +681,54 @@ hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, con
     p.scale_log2 = g.scale_log2;
     if (g.causal) return launch_kernel(attn_step_bf16<true>, p, g.b, g.hq, stream);
     return launch_kernel(attn_step_bf16<false>, p, g.b, g.hq, stream);
+}
+
+hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void *const *k,
+                             const void *const *v, float *const *o, float *const *lse,
+                             hipStream_t stream) {
+    // longest workgroups first: the steps whose query tiles stream the most
+    // key tiles (q_second_half: 2c keys; kv_first_half: c keys), then the
+    // causal step, whose own tiles run from its longest to its shortest
+    int order[CPATTN_MAX_PARTIALS];
+    int m = 0;
+    for (int pass = 0; pass < 3; ++pass)
+        for (int i = 0; i < n; ++i) {
+            const int cls = g[i].causal ? 2 : (g[i].nk >= g[i].nq ? 0 : 1);
+            if (cls == pass) order[m++] = i;
+        }
+    for (int j0 = 0; j0 < n; j0 += MAX_STEPS) {
+        const int nb = n - j0 < MAX_STEPS ? n - j0 : MAX_STEPS;
+        StepsParams sp = {};
+        sp.q = (const uint16_t *)q;
+        sp.two_c = g[0].two_c;
+        sp.hq = g[0].hq;
+        sp.hkv = g[0].hkv;
+        sp.group = g[0].hq / g[0].hkv;
+        sp.scale_log2 = g[0].scale_log2;
+        sp.nsteps = nb;
+        int items = 0;
+        for (int jj = 0; jj < nb; ++jj) {
+            const int i = order[j0 + jj];
+            StepDesc &d = sp.st[jj];
+            d.k = (const uint16_t *)k[i];
+            d.v = (const uint16_t *)v[i];
+            d.o = o[i];
+            d.lse = lse[i];
+            d.q_row0 = (int)g[i].q_row0;
+            d.nq = (int)g[i].nq;
+            d.nk = (int)g[i].nk;
+            d.causal = g[i].causal ? 1 : 0;
+            d.num_qtiles = (int)((g[i].nq + BM - 1) / BM);
+            d.item0 = items;
+            items += d.num_qtiles * sp.group;
+        }
+        sp.items = items;
+        const int64_t blocks = (int64_t)items * sp.hkv * g[0].b;
+        hipLaunchKernelGGL(attn_steps_bf16, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, sp);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz, const void *vz,

@@ -52,6 +52,11 @@ hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const Seq
 hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k,
                             const void *v, float *o, float *lse,
                             hipStream_t stream);
+// Steps 0 .. n-1 of one rank's share (bf16) in one grid: step i reads
+// k[i]/v[i] and writes o[i]/lse[i], as launch_step_bf16 would.
+hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void *const *k,
+                             const void *const *v, float *const *o, float *const *lse,
+                             hipStream_t stream);
 
 // Geometry of one rank's fused share (cpattn_forward_fused[_varlen]).
 struct FusedGeom {

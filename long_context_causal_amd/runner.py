@@ -105,6 +105,12 @@ class CPProblem:
         C.cpattn_step_fwd(self.dims, self.dtype, scale, st["mode"], self.qz[buf["rank"]],
                           self.kz[st["src"]], self.vz[st["src"]], st["o"], st["lse"], stream)
 
+    def steps(self, buf, stream=None, scale=0.0):
+        """All cp steps of the rank's share through cpattn_forward_steps (one
+        grid for bf16), the partials landing in buf's step views."""
+        C.cpattn_forward_steps(self.dims, self.dtype, scale, buf["rank"], self.qz, self.kz,
+                               self.vz, buf["ws"], buf["ws_bytes"], stream)
+
     def merge(self, buf, stream=None):
         parts = [(st["o"], st["lse"], st["row0"], st["rows"]) for st in buf["steps"]]
         C.cpattn_merge(self.dims, parts, buf["out_dtype"], buf["o"], buf["lse"], stream)

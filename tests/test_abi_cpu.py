@@ -157,6 +157,33 @@ def test_forward_workspace_and_validation():
     assert L.cpattn_forward(*args) == C.CPATTN_EINVAL
 
 
+def test_forward_steps_validation():
+    L = C.lib()
+    d = _dims(b=1, s=32768, hq=64, hkv=8, d=128, cp=8)
+    ws = C.cpattn_forward_workspace(d, 3)
+    args = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), 3, ALIGNED, ALIGNED, ALIGNED,
+            ALIGNED, ws - 1, 0]
+    assert L.cpattn_forward_steps(*args) == C.CPATTN_ENOSPACE
+    args[8] = ws
+    args[7] = ALIGNED + 16
+    assert L.cpattn_forward_steps(*args) == C.CPATTN_EALIGN
+    args[7] = ALIGNED
+    args[4] = ALIGNED + 8                          # Q block not 16-byte aligned
+    assert L.cpattn_forward_steps(*args) == C.CPATTN_EALIGN
+    args[4] = ALIGNED
+    args[3] = -1
+    assert L.cpattn_forward_steps(*args) == C.CPATTN_EINVAL
+    args[3] = 3
+    args[2] = ctypes.c_float(float("nan"))
+    assert L.cpattn_forward_steps(*args) == C.CPATTN_EINVAL
+    args[2] = ctypes.c_float(0.0)
+    args[1] = 7
+    assert L.cpattn_forward_steps(*args) == C.CPATTN_EDTYPE
+    args[1] = C.CPATTN_BF16
+    args[6] = None
+    assert L.cpattn_forward_steps(*args) == C.CPATTN_EINVAL
+
+
 def test_binding_names_match_header():
     for name in _declared_functions():
         assert hasattr(C, name), name

@@ -59,22 +59,34 @@ def test_forward_fp32_full_size():
         assert_close(f"rank {r} L", l, l_full[:, :, pos], F32_MAX_ABS)
 
 
-def test_stepwise_calls_equal_forward_entry_point():
-    """The benchmark's per-step calls and cpattn_forward give the same bits."""
-    w = small(WORKLOADS["bf16_gqa_s32k_cp8"], 2 * 8 * 64)
-    say("stepwise vs cpattn_forward")
+@pytest.mark.parametrize("name,s", [("bf16_gqa_s32k_cp8", 2 * 8 * 64),
+                                    ("bf16_gqa_s32k_cp8", 2 * 8 * 300),
+                                    ("bf16_gqa_s128k_cp16_rope", 2 * 16 * 72),
+                                    ("fp32_mha_s512_cp2", 512)])
+def test_stepwise_calls_equal_forward_entry_point(name, s):
+    """One launch per step (cpattn_step_fwd), all steps in one grid
+    (cpattn_forward_steps) and cpattn_forward give the same bits: every
+    partial of every rank, and the merged result."""
+    w = small(WORKLOADS[name], s)
+    say(f"stepwise vs cpattn_forward_steps vs cpattn_forward: {name} s={s}")
     q, k, v = make_inputs(w)
     P = CPProblem(w, q, k, v)
     P.partition()
-    r = w.rank
-    a = P.alloc_rank(r)
-    for i in range(w.cp):
-        P.step(a, i)
-    P.merge(a)
-    b = P.alloc_rank(r)
-    P.forward(b)
-    torch.cuda.synchronize()
-    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+    for r in range(w.cp):
+        a = P.alloc_rank(r)
+        for i in range(w.cp):
+            P.step(a, i)
+        P.merge(a)
+        g = P.alloc_rank(r)
+        g["ws"].fill_(255)            # NaN pattern: every partial must be written
+        P.steps(g)
+        b = P.alloc_rank(r)
+        P.forward(b)
+        torch.cuda.synchronize()
+        for i in range(w.cp):
+            assert torch.equal(a["steps"][i]["o"], g["steps"][i]["o"]), (r, i)
+            assert torch.equal(a["steps"][i]["lse"], g["steps"][i]["lse"]), (r, i)
+        assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"]), r
 
 
 FULL = [("bf16_gqa_s8k_cp4", 12), ("bf16_mha_s16k_cp4_widelogits", 8),

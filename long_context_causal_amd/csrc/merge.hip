@@ -9,10 +9,13 @@
 // Partials that do not cover the row take no part (they are not zeros with
 // L = 0).  All arithmetic is fp32 (exp and log through exp2/log2).
 //
-// One workgroup per (batch, local row): it first computes the hq x n
-// weights exp(L_p - L) into LDS, then streams the hq*d outputs of the row
-// with 16-byte reads of each covering partial (consecutive lanes on
-// consecutive addresses) and one 16-byte (fp32) or 8-byte (bf16) store.
+// One workgroup per (batch, local row): it first gathers the row's L_p of
+// every head into LDS and turns them into the weights exp(L_p - L), then
+// streams the hq*d outputs of the row: each lane owns eight 16-byte vectors
+// (consecutive lanes on consecutive addresses) and, partial by partial,
+// issues their eight reads together before accumulating, so enough reads
+// are in flight to keep HBM busy; one 16-byte (fp32) or 8-byte (bf16) store
+// per vector.
 #include "internal.h"
 
 #include <math.h>
@@ -22,6 +25,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) f32x4 gf32x4;   // global memory
 
 constexpr int NT = 256;
 constexpr int MAX_LDS_WEIGHTS = 8192;   // hq * n must fit (32 KiB)
@@ -41,8 +45,10 @@ template <int NP, bool BF16_OUT>
 __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, int64_t b,
                                                  int64_t two_c, int hq, int d, void *o_out,
                                                  float *lse_out) {
-    __shared__ float w[MAX_LDS_WEIGHTS];   // [hq][n_parts] weights
-    __shared__ int cover[NP];              // indices of the covering partials
+    __shared__ float w[MAX_LDS_WEIGHTS];   // [hq][n_cover]: L_p first, then the weights
+    __shared__ const float *obase[NP];     // covering partial c: its O at (n, row, head 0)
+    __shared__ const float *lbase[NP];     // its L at (n, head 0, row)
+    __shared__ int lstride[NP];            // its L elements between heads (its rows)
     __shared__ int n_cover;
     const int64_t rowid = blockIdx.x;      // n * two_c + j
     const int64_t j = rowid % two_c;
@@ -50,8 +56,15 @@ __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, i
 
     if (threadIdx.x == 0) {
         int cnt = 0;
-        for (int q = 0; q < n_parts; ++q)
-            if (j >= pl.p[q].row0 && j < pl.p[q].row0 + pl.p[q].rows) cover[cnt++] = q;
+        for (int q = 0; q < n_parts; ++q) {
+            const DevPartial &pp = pl.p[q];
+            if (j >= pp.row0 && j < pp.row0 + pp.rows) {
+                obase[cnt] = pp.o + (n * pp.rows + (j - pp.row0)) * (int64_t)hq * d;
+                lbase[cnt] = pp.lse + n * hq * pp.rows + (j - pp.row0);
+                lstride[cnt] = (int)pp.rows;
+                ++cnt;
+            }
+        }
         n_cover = cnt;
     }
     __syncthreads();
@@ -59,56 +72,103 @@ __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, i
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr float LN2 = 0.69314718055994531f;
 
-    for (int h = threadIdx.x; h < hq; h += NT) {
-        float mx = -INFINITY;
-        for (int c = 0; c < nc; ++c) {
-            const DevPartial &pp = pl.p[cover[c]];
-            const float l = pp.lse[(n * hq + h) * pp.rows + (j - pp.row0)];
-            mx = fmaxf(mx, l);
+    // every (head, partial) L into LDS, eight loads in flight per lane
+    // (lanes past the end re-read the last element, so every read is
+    // unconditional and all eight issue before the first wait)
+    const int ne = hq * nc;
+    for (int e0 = 0; e0 < ne; e0 += 8 * NT) {
+        float lv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = min(e0 + k * NT + (int)threadIdx.x, ne - 1);
+            const int h = e / nc, c = e - h * nc;
+            lv[k] = ((const __attribute__((address_space(1))) float *)lbase[c])[(int64_t)h *
+                                                                                  lstride[c]];
         }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = e0 + k * NT + threadIdx.x;
+            if (e < ne) w[e] = lv[k];
+        }
+    }
+    __syncthreads();
+    for (int h = threadIdx.x; h < hq; h += NT) {
+        float *wh = w + h * nc;
+        float mx = -INFINITY;
+        for (int c = 0; c < nc; ++c) mx = fmaxf(mx, wh[c]);
         float total = -INFINITY;
         if (mx != -INFINITY) {
             float ssum = 0.0f;
-            for (int c = 0; c < nc; ++c) {
-                const DevPartial &pp = pl.p[cover[c]];
-                const float l = pp.lse[(n * hq + h) * pp.rows + (j - pp.row0)];
-                ssum += __builtin_amdgcn_exp2f((l - mx) * LOG2E);
-            }
+            for (int c = 0; c < nc; ++c) ssum += __builtin_amdgcn_exp2f((wh[c] - mx) * LOG2E);
             total = mx + __builtin_amdgcn_logf(ssum) * LN2;
         }
-        for (int c = 0; c < nc; ++c) {
-            const DevPartial &pp = pl.p[cover[c]];
-            const float l = pp.lse[(n * hq + h) * pp.rows + (j - pp.row0)];
-            w[h * nc + c] = (total == -INFINITY) ? 0.0f
-                                                 : __builtin_amdgcn_exp2f((l - total) * LOG2E);
-        }
+        for (int c = 0; c < nc; ++c)
+            wh[c] = (total == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((wh[c] - total) * LOG2E);
         if (lse_out != nullptr) lse_out[(n * hq + h) * two_c + j] = total;
     }
     __syncthreads();
 
+    // O: each lane owns KV 16-byte vectors of the row; for every covering
+    // partial the KV loads are issued together, then accumulated.  Full
+    // chunks of KV * NT vectors run unpredicated; the rest one vector at a
+    // time.
+    constexpr int KV = 8;
     const int nvec = hq * d / 4;
     const int vec_per_head = d / 4;
-    for (int i = threadIdx.x; i < nvec; i += NT) {
-        const int h = i / vec_per_head;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int c = 0; c < nc; ++c) {
-            const DevPartial &pp = pl.p[cover[c]];
-            const f32x4 *src =
-                (const f32x4 *)(pp.o + (n * pp.rows + (j - pp.row0)) * (int64_t)hq * d) + i;
-            acc += w[h * nc + c] * (*src);
-        }
+    auto store = [&](int i, const f32x4 &a) {
         if (BF16_OUT) {
             u32x2 packed;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                __bf16 lo = (__bf16)acc[2 * e], hi = (__bf16)acc[2 * e + 1];
+                __bf16 lo = (__bf16)a[2 * e], hi = (__bf16)a[2 * e + 1];
                 packed[e] = (unsigned)__builtin_bit_cast(uint16_t, lo) |
                             ((unsigned)__builtin_bit_cast(uint16_t, hi) << 16);
             }
             ((u32x2 *)o_out)[rowid * nvec + i] = packed;
         } else {
-            ((f32x4 *)o_out)[rowid * nvec + i] = acc;
+            ((f32x4 *)o_out)[rowid * nvec + i] = a;
         }
+    };
+    const int full = nvec / (KV * NT) * (KV * NT);
+    for (int v0 = 0; v0 < full; v0 += KV * NT) {
+        f32x4 acc[KV];
+#pragma unroll
+        for (int k = 0; k < KV; ++k) acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // two partials per round trip: 2 * KV reads in flight per lane
+        int c = 0;
+        for (; c + 1 < nc; c += 2) {
+            const gf32x4 *s0 = (const gf32x4 *)obase[c] + v0 + threadIdx.x;
+            const gf32x4 *s1 = (const gf32x4 *)obase[c + 1] + v0 + threadIdx.x;
+            f32x4 x0[KV], x1[KV];
+#pragma unroll
+            for (int k = 0; k < KV; ++k) x0[k] = s0[k * NT];
+#pragma unroll
+            for (int k = 0; k < KV; ++k) x1[k] = s1[k * NT];
+#pragma unroll
+            for (int k = 0; k < KV; ++k) {
+                const int wi = ((v0 + k * NT + threadIdx.x) / vec_per_head) * nc + c;
+                acc[k] += w[wi] * x0[k] + w[wi + 1] * x1[k];
+            }
+        }
+        if (c < nc) {
+            const gf32x4 *s0 = (const gf32x4 *)obase[c] + v0 + threadIdx.x;
+            f32x4 x0[KV];
+#pragma unroll
+            for (int k = 0; k < KV; ++k) x0[k] = s0[k * NT];
+#pragma unroll
+            for (int k = 0; k < KV; ++k) {
+                const int wi = ((v0 + k * NT + threadIdx.x) / vec_per_head) * nc + c;
+                acc[k] += w[wi] * x0[k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KV; ++k) store(v0 + k * NT + threadIdx.x, acc[k]);
+    }
+    for (int i = full + threadIdx.x; i < nvec; i += NT) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = 0; c < nc; ++c)
+            acc += w[(i / vec_per_head) * nc + c] * ((const f32x4 *)obase[c])[i];
+        store(i, acc);
     }
 }
 

@@ -430,15 +430,32 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
     if (e == hipSuccess) e = cpattn::launch_bwd_delta(dims->b, two_c, dims->hq, o_r, do_r,
                                                       delta_ws, s);
     if (e != hipSuccess) return CPATTN_EHIP;
+    // unpacked: every step's dK/dV in one grid (each step owns its source
+    // block's contribution), dq step by step; packed samples: both per step
+    const bool one_grid = t.nseq == 1;
+    StepGeom geo[CPATTN_MAX_PARTIALS];
+    int modes[CPATTN_MAX_PARTIALS];
+    const void *ks[CPATTN_MAX_PARTIALS], *vs[CPATTN_MAX_PARTIALS];
+    float *dks[CPATTN_MAX_PARTIALS], *dvs[CPATTN_MAX_PARTIALS];
     for (int i = 0; i < dims->cp; ++i) {
         int mode, src;
         cpattn_step_mode(i, rank, dims->cp, &mode, &src);
         // ring hand-off: step i reads rank src's K/V and adds to src's dK/dV
         const char *k_src = (const char *)kz + src * kv_elems * 2;
         const char *v_src = (const char *)vz + src * kv_elems * 2;
-        const StepGeom g = cpattn::step_geom(*dims, mode, scale);
-        e = cpattn::launch_step_bwd_bf16(g, t, mode, q_r, k_src, v_src, do_r, lse_r, delta_ws,
-                                         dq_r, dkz + src * kv_elems, dvz + src * kv_elems, s);
+        geo[i] = cpattn::step_geom(*dims, mode, scale);
+        modes[i] = mode;
+        ks[i] = k_src;
+        vs[i] = v_src;
+        dks[i] = dkz + src * kv_elems;
+        dvs[i] = dvz + src * kv_elems;
+        e = cpattn::launch_step_bwd_bf16(geo[i], t, mode, q_r, k_src, v_src, do_r, lse_r,
+                                         delta_ws, dq_r, dks[i], dvs[i], s, !one_grid);
+        if (e != hipSuccess) return CPATTN_EHIP;
+    }
+    if (one_grid) {
+        e = cpattn::launch_bwd_dkdv_steps_bf16(dims->cp, geo, modes, q_r, ks, vs, do_r, lse_r,
+                                               delta_ws, dks, dvs, s);
         if (e != hipSuccess) return CPATTN_EHIP;
     }
     return CPATTN_OK;

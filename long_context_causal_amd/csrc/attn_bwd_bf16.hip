@@ -74,14 +74,14 @@ struct Geo {
     int qrow0, kv0, nq, nk;
     bool causal;
 };
-__device__ __forceinline__ Geo geo_of(const BwdParams &p, int i) {
+__device__ __forceinline__ Geo geo_of(const BwdParams &p, int i, int mode) {
     const int l0 = p.tab.lcu[i], c = (p.tab.lcu[i + 1] - l0) >> 1;
     Geo G;
     G.kv0 = l0;
-    G.causal = p.mode == CPATTN_CAUSAL;
-    G.qrow0 = p.mode == CPATTN_Q_SECOND_HALF ? l0 + c : l0;
-    G.nq = p.mode == CPATTN_Q_SECOND_HALF ? c : 2 * c;
-    G.nk = p.mode == CPATTN_KV_FIRST_HALF ? c : 2 * c;
+    G.causal = mode == CPATTN_CAUSAL;
+    G.qrow0 = mode == CPATTN_Q_SECOND_HALF ? l0 + c : l0;
+    G.nq = mode == CPATTN_Q_SECOND_HALF ? c : 2 * c;
+    G.nk = mode == CPATTN_KV_FIRST_HALF ? c : 2 * c;
     return G;
 }
 
@@ -190,15 +190,24 @@ attn_bwd_dq(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
+    // workgroup -> (head in group, query tile, KV group, batch), fastest
+    // first.  The dispatcher deals workgroups to the 8 XCDs round robin;
+    // reordered so each XCD takes a contiguous run (the heads of a KV group,
+    // which stream the same K/V, share its L2), and inside the run the
+    // longest (causal: last) query tiles start first.
     int item = blockIdx.x;
+    const int nblk = gridDim.x;
+    if ((nblk & 7) == 0) item = (item & 7) * (nblk >> 3) + (item >> 3);
     const int nqt = p.tab.tile0[p.tab.nseq];   // query tiles of all samples
-    const int qt_all = nqt - 1 - item % nqt;   // longest (causal) tiles first
+    const int hh = item % p.group;
+    item /= p.group;
+    const int qt_all = nqt - 1 - item % nqt;
     item /= nqt;
-    const int head = item % p.hq;
-    const int n = item / p.hq;
-    const int g = head / p.group;
+    const int g = item % p.hkv;
+    const int n = item / p.hkv;
+    const int head = g * p.group + hh;
     const int smp = seq_of(p.tab.tile0, p.tab.nseq, qt_all);
-    const Geo G = geo_of(p, smp);
+    const Geo G = geo_of(p, smp, p.mode);
     const int qt = qt_all - p.tab.tile0[smp];
     const int q0 = qt * TR * NWB;
     const int wrow0 = q0 + wave * TR;
@@ -354,27 +363,36 @@ constexpr int STAGE_DKDV = 2 * TB + NWK * LD_SLOT;   // Q, dO, L/D slots
 constexpr int PSLAB = 64 * 16 * 4;             // one key group's fp32 P of a tile
 constexpr int DKDV_LDS = NSK * STAGE_DKDV + 2 * KW * PSLAB;
 
-__global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bwd_dkdv(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
+// What a dK/dV workgroup takes from its step: the source block's K and V,
+// where its dK and dV go, the mode, and over how many workgroups the
+// group's heads are split.
+struct KvStep {
+    const uint16_t *k, *v;
+    float *dk, *dv;
+    int mode, head_splits;
+};
+
+// The dK/dV workgroup 'item' of one step (item as blockIdx.x of that
+// step's own launch).
+__device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, int item,
+                                          char *lds) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool ds_wave = wave >= KW;           // wave-uniform role
     const int kwave = wave & (KW - 1);
     const int hi = lane >> 5, l32 = lane & 31;
     // longest (causal: first) key blocks are dispatched first
-    int item = blockIdx.x;
-    const int inner = p.head_splits * p.hkv * p.b;
+    const int inner = io.head_splits * p.hkv * p.b;
     const int kt_all = item / inner;
     const int smp = seq_of(p.tab.tile0, p.tab.nseq, kt_all);
-    const Geo G = geo_of(p, smp);
+    const Geo G = geo_of(p, smp, io.mode);
     const int kt = kt_all - p.tab.tile0[smp];
     item %= inner;
-    const int hs = item % p.head_splits;
-    item /= p.head_splits;
+    const int hs = item % io.head_splits;
+    item /= io.head_splits;
     const int g = item % p.hkv;
     const int n = item / p.hkv;
-    const int hpw = p.group / p.head_splits;   // query heads of this workgroup
+    const int hpw = p.group / io.head_splits;   // query heads of this workgroup
     const int h0 = g * p.group + hs * hpw;
     const int k0 = kt * TR * KW;
     const int wkey0 = k0 + kwave * TR;
@@ -388,7 +406,7 @@ attn_bwd_dkdv(BwdParams p) {
     const int kr = min(key, G.nk - 1);
     const int64_t koff = ((n * p.two_c + G.kv0 + kr) * (int64_t)p.hkv + g) * D;
     bf16x8 bf[D / 16];
-    load_b_rows((ds_wave ? p.v : p.k) + koff, hi, bf);
+    load_b_rows((ds_wave ? io.v : io.k) + koff, hi, bf);
     settle(bf);
     f32x16 acc[D / 32];
 #pragma unroll
@@ -529,9 +547,9 @@ attn_bwd_dkdv(BwdParams p) {
     // dv += dV (P waves), dk += scale dK (dS waves); lane holds head dims
     // dt*32 + 8*i + 4*hi + j.  Split heads add with atomics.
     if (key < G.nk && ntiles > 0) {
-        float *dst = (ds_wave ? p.dk : p.dv) + koff + 4 * hi;
+        float *dst = (ds_wave ? io.dk : io.dv) + koff + 4 * hi;
         const float f = ds_wave ? p.scale : 1.0f;
-        if (p.head_splits == 1) {
+        if (io.head_splits == 1) {
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -552,6 +570,41 @@ attn_bwd_dkdv(BwdParams p) {
                         unsafeAtomicAdd(dst + dt * 32 + i * 8 + j, f * acc[dt][i * 4 + j]);
         }
     }
+}
+
+// One step's dK/dV.
+__global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
+    dkdv_item(p, KvStep{p.k, p.v, p.dk, p.dv, p.mode, p.head_splits}, blockIdx.x, lds);
+}
+
+// The dK/dV of several steps of one rank's (unpacked) share in one grid.
+// Each step reads its own source block and writes that block's dK/dV
+// contribution, which no other step of the share touches, so a workgroup
+// takes all query heads of its KV group (no head split, no atomics) and the
+// steps' workgroups share the machine instead of running in rounds of
+// equal workgroups.  The host orders the steps longest workgroups first.
+constexpr int MAX_BWD_STEPS = 32;
+struct KvStepDesc {
+    const uint16_t *k, *v;
+    float *dk, *dv;
+    int mode, item0;          // first workgroup of the step in the grid
+};
+struct DkdvStepsParams {
+    BwdParams p;              // the rank's Q side, dims, scale, one-sample table
+    int nsteps;
+    KvStepDesc st[MAX_BWD_STEPS];
+};
+
+__global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv_steps(DkdvStepsParams sp) {
+    __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
+    const int item = blockIdx.x;
+    int j = 0;
+    while (j + 1 < sp.nsteps && sp.st[j + 1].item0 <= item) ++j;
+    const KvStepDesc &d = sp.st[j];
+    dkdv_item(sp.p, KvStep{d.k, d.v, d.dk, d.dv, d.mode, 1}, item - d.item0, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -605,10 +658,10 @@ hipError_t launch_fill_zero(float *x, int64_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode,
-                                const void *q, const void *k, const void *v, const void *dout,
-                                const float *lse, const float *delta, float *dq, float *dk,
-                                float *dv, hipStream_t stream) {
+namespace {
+BwdParams make_params(const StepGeom &g, const SeqTable &tab, int mode, const void *q,
+                      const void *k, const void *v, const void *dout, const float *lse,
+                      const float *delta, float *dq, float *dk, float *dv) {
     BwdParams p = {};
     p.q = (const uint16_t *)q;
     p.k = (const uint16_t *)k;
@@ -628,26 +681,37 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
     p.scale_log2 = g.scale_log2;
     p.mode = mode;
     p.tab = tab;
-    // each sample's query rows (dq: tiles of TR * NWB rows) and keys (dK/dV:
-    // tiles of TR * KW keys) in this mode
-    auto fill_tiles = [&](bool keys, int per_tile) {
-        p.tab.tile0[0] = 0;
-        for (int i = 0; i < tab.nseq; ++i) {
-            const int c = (tab.lcu[i + 1] - tab.lcu[i]) / 2;
-            const int n = keys ? (mode == CPATTN_KV_FIRST_HALF ? c : 2 * c)
-                               : (mode == CPATTN_Q_SECOND_HALF ? c : 2 * c);
-            p.tab.tile0[i + 1] = p.tab.tile0[i] + (n + per_tile - 1) / per_tile;
-        }
-        return (int64_t)p.tab.tile0[tab.nseq];
-    };
-    const int64_t nqt = fill_tiles(false, TR * NWB);
+    return p;
+}
+
+// each sample's query rows (dq: tiles of TR * NWB rows) or keys (dK/dV:
+// tiles of TR * KW keys) in this mode, into p.tab.tile0; returns the total
+int64_t fill_tiles(BwdParams &p, const SeqTable &tab, int mode, bool keys) {
+    const int per_tile = keys ? TR * KW : TR * NWB;
+    p.tab.tile0[0] = 0;
+    for (int i = 0; i < tab.nseq; ++i) {
+        const int c = (tab.lcu[i + 1] - tab.lcu[i]) / 2;
+        const int n = keys ? (mode == CPATTN_KV_FIRST_HALF ? c : 2 * c)
+                           : (mode == CPATTN_Q_SECOND_HALF ? c : 2 * c);
+        p.tab.tile0[i + 1] = p.tab.tile0[i] + (n + per_tile - 1) / per_tile;
+    }
+    return (int64_t)p.tab.tile0[tab.nseq];
+}
+}  // namespace
+
+hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode,
+                                const void *q, const void *k, const void *v, const void *dout,
+                                const float *lse, const float *delta, float *dq, float *dk,
+                                float *dv, hipStream_t stream, bool with_dkdv) {
+    BwdParams p = make_params(g, tab, mode, q, k, v, dout, lse, delta, dq, dk, dv);
+    const int64_t nqt = fill_tiles(p, tab, mode, false);
     hipLaunchKernelGGL(attn_bwd_dq, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * NWB), 0,
                        stream, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !with_dkdv) return e;
     // the group's heads split so the grid has at least ~2 workgroups per CU
     // (heads per workgroup divides the group)
-    const int64_t base_wgs = fill_tiles(true, TR * KW) * g.hkv * g.b;
+    const int64_t base_wgs = fill_tiles(p, tab, mode, true) * g.hkv * g.b;
     p.head_splits = 1;
     while (p.head_splits < p.group && p.group % (p.head_splits * 2) == 0 &&
            base_wgs * p.head_splits < 512)
@@ -655,6 +719,54 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
     hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)(base_wgs * p.head_splits)),
                        dim3(64 * NWK), 0, stream, p);
     return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const int *mode,
+                                      const void *q, const void *const *k,
+                                      const void *const *v, const void *dout,
+                                      const float *lse, const float *delta, float *const *dk,
+                                      float *const *dv, hipStream_t stream) {
+    // one sample per batch element: the table is [0, 2c)
+    SeqTable tab = {};
+    tab.nseq = 1;
+    tab.lcu[1] = (int32_t)g[0].two_c;
+    // longest workgroups first: kv_first_half key tiles (every query row),
+    // q_second_half tiles (the second chunk's rows), then the causal step
+    // (its first key tiles see the most rows)
+    int order[CPATTN_MAX_PARTIALS];
+    int m = 0;
+    for (int pass = 0; pass < 3; ++pass)
+        for (int i = 0; i < n; ++i) {
+            const int cls = mode[i] == CPATTN_KV_FIRST_HALF ? 0
+                            : mode[i] == CPATTN_Q_SECOND_HALF ? 1 : 2;
+            if (cls == pass) order[m++] = i;
+        }
+    for (int j0 = 0; j0 < n; j0 += MAX_BWD_STEPS) {
+        const int nb = n - j0 < MAX_BWD_STEPS ? n - j0 : MAX_BWD_STEPS;
+        DkdvStepsParams sp = {};
+        sp.p = make_params(g[0], tab, CPATTN_CAUSAL, q, nullptr, nullptr, dout, lse, delta,
+                           nullptr, nullptr, nullptr);
+        sp.nsteps = nb;
+        int64_t items = 0;
+        for (int jj = 0; jj < nb; ++jj) {
+            const int i = order[j0 + jj];
+            KvStepDesc &d = sp.st[jj];
+            d.k = (const uint16_t *)k[i];
+            d.v = (const uint16_t *)v[i];
+            d.dk = dk[i];
+            d.dv = dv[i];
+            d.mode = mode[i];
+            d.item0 = (int)items;
+            const int64_t c = g[0].two_c / 2;
+            const int64_t nk = mode[i] == CPATTN_KV_FIRST_HALF ? c : 2 * c;
+            items += (nk + TR * KW - 1) / (TR * KW) * g[0].hkv * g[0].b;
+        }
+        hipLaunchKernelGGL(attn_bwd_dkdv_steps, dim3((unsigned)items), dim3(64 * NWK), 0,
+                           stream, sp);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace cpattn

@@ -80,7 +80,15 @@ hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
 hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode,
                                 const void *q, const void *k, const void *v, const void *dout,
                                 const float *lse, const float *delta, float *dq, float *dk,
-                                float *dv, hipStream_t stream);
+                                float *dv, hipStream_t stream, bool with_dkdv = true);
+// The dK/dV of steps 0 .. n-1 of one rank's unpacked share in one grid:
+// step i reads k[i]/v[i] and adds to dk[i]/dv[i] (distinct blocks, zeroed
+// by the caller), mode[i] its mode; g[0] supplies the dims and scale.
+hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const int *mode,
+                                      const void *q, const void *const *k,
+                                      const void *const *v, const void *dout,
+                                      const float *lse, const float *delta, float *const *dk,
+                                      float *const *dv, hipStream_t stream);
 
 // delta[n, h, i] = sum_t dout[n, i, h, t] o[n, i, h, t]; o fp32, dout bf16.
 hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o,

@@ -430,9 +430,8 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
     if (e == hipSuccess) e = cpattn::launch_bwd_delta(dims->b, two_c, dims->hq, o_r, do_r,
                                                       delta_ws, s);
     if (e != hipSuccess) return CPATTN_EHIP;
-    // unpacked: every step's dK/dV in one grid (each step owns its source
-    // block's contribution), dq step by step; packed samples: both per step
-    const bool one_grid = t.nseq == 1;
+    // every step's dK/dV in one grid (each step owns its source block's
+    // contribution), dq step by step
     StepGeom geo[CPATTN_MAX_PARTIALS];
     int modes[CPATTN_MAX_PARTIALS];
     const void *ks[CPATTN_MAX_PARTIALS], *vs[CPATTN_MAX_PARTIALS];
@@ -450,14 +449,12 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
         dks[i] = dkz + src * kv_elems;
         dvs[i] = dvz + src * kv_elems;
         e = cpattn::launch_step_bwd_bf16(geo[i], t, mode, q_r, k_src, v_src, do_r, lse_r,
-                                         delta_ws, dq_r, dks[i], dvs[i], s, !one_grid);
+                                         delta_ws, dq_r, dks[i], dvs[i], s, false);
         if (e != hipSuccess) return CPATTN_EHIP;
     }
-    if (one_grid) {
-        e = cpattn::launch_bwd_dkdv_steps_bf16(dims->cp, geo, modes, q_r, ks, vs, do_r, lse_r,
-                                               delta_ws, dks, dvs, s);
-        if (e != hipSuccess) return CPATTN_EHIP;
-    }
+    e = cpattn::launch_bwd_dkdv_steps_bf16(dims->cp, geo, t, modes, q_r, ks, vs, do_r, lse_r,
+                                           delta_ws, dks, dvs, s);
+    if (e != hipSuccess) return CPATTN_EHIP;
     return CPATTN_OK;
 }
 

@@ -370,6 +370,7 @@ struct KvStep {
     const uint16_t *k, *v;
     float *dk, *dv;
     int mode, head_splits;
+    const int32_t *tile0;   // first key tile of each sample in this mode
 };
 
 // The dK/dV workgroup 'item' of one step (item as blockIdx.x of that
@@ -384,9 +385,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
     // longest (causal: first) key blocks are dispatched first
     const int inner = io.head_splits * p.hkv * p.b;
     const int kt_all = item / inner;
-    const int smp = seq_of(p.tab.tile0, p.tab.nseq, kt_all);
+    const int smp = seq_of(io.tile0, p.tab.nseq, kt_all);
     const Geo G = geo_of(p, smp, io.mode);
-    const int kt = kt_all - p.tab.tile0[smp];
+    const int kt = kt_all - io.tile0[smp];
     item %= inner;
     const int hs = item % io.head_splits;
     item /= io.head_splits;
@@ -576,15 +577,19 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
 __global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
-    dkdv_item(p, KvStep{p.k, p.v, p.dk, p.dv, p.mode, p.head_splits}, blockIdx.x, lds);
+    dkdv_item(p, KvStep{p.k, p.v, p.dk, p.dv, p.mode, p.head_splits, p.tab.tile0}, blockIdx.x,
+              lds);
 }
 
-// The dK/dV of several steps of one rank's (unpacked) share in one grid.
-// Each step reads its own source block and writes that block's dK/dV
-// contribution, which no other step of the share touches, so a workgroup
-// takes all query heads of its KV group (no head split, no atomics) and the
-// steps' workgroups share the machine instead of running in rounds of
-// equal workgroups.  The host orders the steps longest workgroups first.
+// The dK/dV of several steps of one rank's share in one grid.  Each step
+// reads its own source block and writes that block's dK/dV contribution,
+// which no other step of the share touches, so a workgroup takes all query
+// heads of its KV group (no head split, no atomics) and the steps'
+// workgroups share the machine instead of running in rounds of equal
+// workgroups.  The host orders the steps longest workgroups first.  The
+// key tiles of packed samples are numbered sample by sample: p.tab.tile0
+// for the modes that see 2c keys of a sample, tile0_half for
+// kv_first_half (c keys).
 constexpr int MAX_BWD_STEPS = 32;
 struct KvStepDesc {
     const uint16_t *k, *v;
@@ -592,7 +597,8 @@ struct KvStepDesc {
     int mode, item0;          // first workgroup of the step in the grid
 };
 struct DkdvStepsParams {
-    BwdParams p;              // the rank's Q side, dims, scale, one-sample table
+    BwdParams p;              // the rank's Q side, dims, scale, sample table
+    int32_t tile0_half[CPATTN_MAX_SEQS + 1];
     int nsteps;
     KvStepDesc st[MAX_BWD_STEPS];
 };
@@ -604,7 +610,10 @@ attn_bwd_dkdv_steps(DkdvStepsParams sp) {
     int j = 0;
     while (j + 1 < sp.nsteps && sp.st[j + 1].item0 <= item) ++j;
     const KvStepDesc &d = sp.st[j];
-    dkdv_item(sp.p, KvStep{d.k, d.v, d.dk, d.dv, d.mode, 1}, item - d.item0, lds);
+    dkdv_item(sp.p,
+              KvStep{d.k, d.v, d.dk, d.dv, d.mode, 1,
+                     d.mode == CPATTN_KV_FIRST_HALF ? sp.tile0_half : sp.p.tab.tile0},
+              item - d.item0, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -721,15 +730,11 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const int *mode,
-                                      const void *q, const void *const *k,
+hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &tab,
+                                      const int *mode, const void *q, const void *const *k,
                                       const void *const *v, const void *dout,
                                       const float *lse, const float *delta, float *const *dk,
                                       float *const *dv, hipStream_t stream) {
-    // one sample per batch element: the table is [0, 2c)
-    SeqTable tab = {};
-    tab.nseq = 1;
-    tab.lcu[1] = (int32_t)g[0].two_c;
     // longest workgroups first: kv_first_half key tiles (every query row),
     // q_second_half tiles (the second chunk's rows), then the causal step
     // (its first key tiles see the most rows)
@@ -746,6 +751,10 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const int *mode,
         DkdvStepsParams sp = {};
         sp.p = make_params(g[0], tab, CPATTN_CAUSAL, q, nullptr, nullptr, dout, lse, delta,
                            nullptr, nullptr, nullptr);
+        const int64_t kt_full = fill_tiles(sp.p, tab, CPATTN_CAUSAL, true);
+        BwdParams half = sp.p;
+        const int64_t kt_half = fill_tiles(half, tab, CPATTN_KV_FIRST_HALF, true);
+        for (int i = 0; i <= tab.nseq; ++i) sp.tile0_half[i] = half.tab.tile0[i];
         sp.nsteps = nb;
         int64_t items = 0;
         for (int jj = 0; jj < nb; ++jj) {
@@ -757,9 +766,7 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const int *mode,
             d.dv = dv[i];
             d.mode = mode[i];
             d.item0 = (int)items;
-            const int64_t c = g[0].two_c / 2;
-            const int64_t nk = mode[i] == CPATTN_KV_FIRST_HALF ? c : 2 * c;
-            items += (nk + TR * KW - 1) / (TR * KW) * g[0].hkv * g[0].b;
+            items += (mode[i] == CPATTN_KV_FIRST_HALF ? kt_half : kt_full) * g[0].hkv * g[0].b;
         }
         hipLaunchKernelGGL(attn_bwd_dkdv_steps, dim3((unsigned)items), dim3(64 * NWK), 0,
                            stream, sp);

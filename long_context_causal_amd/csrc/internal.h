@@ -81,10 +81,12 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
                                 const void *q, const void *k, const void *v, const void *dout,
                                 const float *lse, const float *delta, float *dq, float *dk,
                                 float *dv, hipStream_t stream, bool with_dkdv = true);
-// The dK/dV of steps 0 .. n-1 of one rank's unpacked share in one grid:
-// step i reads k[i]/v[i] and adds to dk[i]/dv[i] (distinct blocks, zeroed
-// by the caller), mode[i] its mode; g[0] supplies the dims and scale.
-hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const int *mode,
+// The dK/dV of steps 0 .. n-1 of one rank's share in one grid: step i
+// reads k[i]/v[i] and adds to dk[i]/dv[i] (distinct blocks, zeroed by the
+// caller), mode[i] its mode; g[0] supplies the dims and scale, tab the
+// packed samples.
+hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &tab,
+                                      const int *mode,
                                       const void *q, const void *const *k,
                                       const void *const *v, const void *dout,
                                       const float *lse, const float *delta, float *const *dk,

@@ -15,6 +15,8 @@ gradients are sums with cancellation, so the error is measured against
 the gradient's own scale): max |err| <= 1e-2 * max |ref| and mean |err|
 <= 5e-3 * mean |ref|, per gradient.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -55,9 +57,15 @@ REDUCED = [("bf16_gqa_s32k_cp8", 2 * 8 * 64), ("bf16_gqa_s8k_cp4", 2 * 4 * 100),
            ("bf16_mha_s16k_cp4_widelogits", 2 * 4 * 96), ("bf16_gqa_s128k_cp16_rope", 2 * 16 * 24)]
 
 
-@pytest.mark.parametrize("name,s", REDUCED)
+# more steps than one grid launch takes (32): the one-grid dK/dV runs in
+# two launches
+WIDE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp40", s=2 * 40 * 40,
+                              hq=4, hkv=2, cp=40)
+
+
+@pytest.mark.parametrize("name,s", REDUCED + [("cp40", WIDE_CP.s)])
 def test_backward_all_ranks_reduced(name, s):
-    w = small(WORKLOADS[name], s)
+    w = WIDE_CP if name == "cp40" else small(WORKLOADS[name], s)
     say(f"backward reduced {name} s={s}")
     q, k, v = make_inputs(w)
     do = _dout(w)

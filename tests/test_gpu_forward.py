@@ -7,6 +7,8 @@
   benchmark times: sampled rows (chunk edges plus random rows) of every
   rank (the RoPE workload: its measured rank) vs the oracle row by row.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -16,6 +18,11 @@ from gpu_helpers import (BF16_MAX_ABS, BF16_MEAN_ABS, F32_MAX_ABS, C, CPProblem,
 from long_context_causal_amd.inputs import WORKLOADS
 
 pytestmark = pytest.mark.gpu
+
+# more steps than one grid launch takes (32): the steps run in two grids
+WIDE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp40", s=2 * 40 * 40,
+                              hq=4, hkv=2, cp=40)
+
 
 REDUCED = [("fp32_mha_s512_cp2", 2 * 2 * 77, None),
            ("bf16_gqa_s8k_cp4", 2 * 4 * 100, None),
@@ -45,6 +52,21 @@ def test_forward_reduced_all_ranks(name, s, b):
         assert_close(f"rank {r} L", l, l_full[:, :, pos], 1e-3 if w.dtype == "bf16" else 1e-5)
 
 
+def test_forward_wide_cp_all_ranks():
+    """cp = 40: more steps than one grid launch takes, ragged chunks (c = 40)."""
+    w = WIDE_CP
+    say(f"forward cp={w.cp} s={w.s}")
+    q, k, v = make_inputs(w)
+    o_full, l_full = oracle_full(w, q, k, v)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    for r in range(w.cp):
+        o, l = run_rank(P, r)
+        pos = ocp.zigzag_positions(w.s, w.cp, r)
+        assert_close(f"rank {r} O", o, o_full[:, pos], BF16_MAX_ABS, BF16_MEAN_ABS)
+        assert_close(f"rank {r} L", l, l_full[:, :, pos], 1e-3)
+
+
 def test_forward_fp32_full_size():
     w = WORKLOADS["fp32_mha_s512_cp2"]
     say(f"forward full {w.name}")
@@ -62,12 +84,13 @@ def test_forward_fp32_full_size():
 @pytest.mark.parametrize("name,s", [("bf16_gqa_s32k_cp8", 2 * 8 * 64),
                                     ("bf16_gqa_s32k_cp8", 2 * 8 * 300),
                                     ("bf16_gqa_s128k_cp16_rope", 2 * 16 * 72),
-                                    ("fp32_mha_s512_cp2", 512)])
+                                    ("fp32_mha_s512_cp2", 512),
+                                    ("cp40", WIDE_CP.s)])
 def test_stepwise_calls_equal_forward_entry_point(name, s):
     """One launch per step (cpattn_step_fwd), all steps in one grid
     (cpattn_forward_steps) and cpattn_forward give the same bits: every
     partial of every rank, and the merged result."""
-    w = small(WORKLOADS[name], s)
+    w = WIDE_CP if name == "cp40" else small(WORKLOADS[name], s)
     say(f"stepwise vs cpattn_forward_steps vs cpattn_forward: {name} s={s}")
     q, k, v = make_inputs(w)
     P = CPProblem(w, q, k, v)

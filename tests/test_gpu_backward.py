@@ -61,11 +61,14 @@ REDUCED = [("bf16_gqa_s32k_cp8", 2 * 8 * 64), ("bf16_gqa_s8k_cp4", 2 * 4 * 100),
 # two launches
 WIDE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp40", s=2 * 40 * 40,
                               hq=4, hkv=2, cp=40)
+ONE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp1", s=400, hq=4,
+                             hkv=2, cp=1)
+EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP}
 
 
-@pytest.mark.parametrize("name,s", REDUCED + [("cp40", WIDE_CP.s)])
+@pytest.mark.parametrize("name,s", REDUCED + [("cp40", WIDE_CP.s), ("cp1", ONE_CP.s)])
 def test_backward_all_ranks_reduced(name, s):
-    w = WIDE_CP if name == "cp40" else small(WORKLOADS[name], s)
+    w = EXTRA[name] if name in EXTRA else small(WORKLOADS[name], s)
     say(f"backward reduced {name} s={s}")
     q, k, v = make_inputs(w)
     do = _dout(w)

@@ -22,6 +22,10 @@ pytestmark = pytest.mark.gpu
 # more steps than one grid launch takes (32): the steps run in two grids
 WIDE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp40", s=2 * 40 * 40,
                               hq=4, hkv=2, cp=40)
+# one rank: the share is the causal step alone (c = 200, ragged)
+ONE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp1", s=400, hq=4,
+                             hkv=2, cp=1)
+EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP}
 
 
 REDUCED = [("fp32_mha_s512_cp2", 2 * 2 * 77, None),
@@ -52,9 +56,11 @@ def test_forward_reduced_all_ranks(name, s, b):
         assert_close(f"rank {r} L", l, l_full[:, :, pos], 1e-3 if w.dtype == "bf16" else 1e-5)
 
 
-def test_forward_wide_cp_all_ranks():
-    """cp = 40: more steps than one grid launch takes, ragged chunks (c = 40)."""
-    w = WIDE_CP
+@pytest.mark.parametrize("name", sorted(EXTRA))
+def test_forward_extreme_cp_all_ranks(name):
+    """cp = 40 (more steps than one grid launch takes, ragged chunks c = 40)
+    and cp = 1 (the causal step alone)."""
+    w = EXTRA[name]
     say(f"forward cp={w.cp} s={w.s}")
     q, k, v = make_inputs(w)
     o_full, l_full = oracle_full(w, q, k, v)
@@ -85,12 +91,12 @@ def test_forward_fp32_full_size():
                                     ("bf16_gqa_s32k_cp8", 2 * 8 * 300),
                                     ("bf16_gqa_s128k_cp16_rope", 2 * 16 * 72),
                                     ("fp32_mha_s512_cp2", 512),
-                                    ("cp40", WIDE_CP.s)])
+                                    ("cp40", WIDE_CP.s), ("cp1", ONE_CP.s)])
 def test_stepwise_calls_equal_forward_entry_point(name, s):
     """One launch per step (cpattn_step_fwd), all steps in one grid
     (cpattn_forward_steps) and cpattn_forward give the same bits: every
     partial of every rank, and the merged result."""
-    w = WIDE_CP if name == "cp40" else small(WORKLOADS[name], s)
+    w = EXTRA[name] if name in EXTRA else small(WORKLOADS[name], s)
     say(f"stepwise vs cpattn_forward_steps vs cpattn_forward: {name} s={s}")
     q, k, v = make_inputs(w)
     P = CPProblem(w, q, k, v)

@@ -424,14 +424,14 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
     const int64_t q_elems = dims->b * two_c * dims->hq * dims->d;
     const int64_t kv_elems = dims->b * two_c * dims->hkv * dims->d;
     const char *q_r = (const char *)qz + rank * q_elems * 2;
-    hipError_t e = cpattn::launch_fill_zero(dq_r, q_elems, s);
-    if (e == hipSuccess) e = cpattn::launch_fill_zero(dkz, kv_elems * dims->cp, s);
+    hipError_t e = cpattn::launch_fill_zero(dkz, kv_elems * dims->cp, s);
     if (e == hipSuccess) e = cpattn::launch_fill_zero(dvz, kv_elems * dims->cp, s);
     if (e == hipSuccess) e = cpattn::launch_bwd_delta(dims->b, two_c, dims->hq, o_r, do_r,
                                                       delta_ws, s);
     if (e != hipSuccess) return CPATTN_EHIP;
-    // every step's dK/dV in one grid (each step owns its source block's
-    // contribution), dq step by step
+    // every step's dq in one grid (a workgroup streams all steps' keys for
+    // its query rows and writes dq once), then every step's dK/dV in one
+    // grid (each step owns its source block's contribution)
     StepGeom geo[CPATTN_MAX_PARTIALS];
     int modes[CPATTN_MAX_PARTIALS];
     const void *ks[CPATTN_MAX_PARTIALS], *vs[CPATTN_MAX_PARTIALS];
@@ -448,10 +448,10 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
         vs[i] = v_src;
         dks[i] = dkz + src * kv_elems;
         dvs[i] = dvz + src * kv_elems;
-        e = cpattn::launch_step_bwd_bf16(geo[i], t, mode, q_r, k_src, v_src, do_r, lse_r,
-                                         delta_ws, dq_r, dks[i], dvs[i], s, false);
-        if (e != hipSuccess) return CPATTN_EHIP;
     }
+    e = cpattn::launch_bwd_dq_share_bf16(geo[0], t, rank, dims->cp, q_r, kz, vz, do_r, lse_r,
+                                         delta_ws, dq_r, s);
+    if (e != hipSuccess) return CPATTN_EHIP;
     e = cpattn::launch_bwd_dkdv_steps_bf16(dims->cp, geo, t, modes, q_r, ks, vs, do_r, lse_r,
                                            delta_ws, dks, dvs, s);
     if (e != hipSuccess) return CPATTN_EHIP;

@@ -63,6 +63,10 @@ struct BwdParams {
     int b, hq, hkv, group, head_splits;
     float scale, scale_log2;
     int mode;                           // the step's mode (same for every sample)
+    // the rank's whole share in one grid (dq): k, v are rank 0's blocks of
+    // the partitioned K, V, block_elems apart
+    int rank, cp;
+    int64_t block_elems;
     SeqTable tab;                       // packed samples; tile0: this kernel's tiles
 };
 
@@ -184,9 +188,99 @@ constexpr int NSQ = 4;
 constexpr int PDQ = NSQ - 1;
 constexpr int STAGE_DQ = 2 * TB;           // K, V
 
-__global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bwd_dq(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
+// A run of 32-key tiles a dQ workgroup streams for its query rows: the K, V
+// base of the block (this batch element and KV head, at the sample's first
+// key), the tile's first key, the keys of the block visible in the segment,
+// whether the causal mask applies (key <= row, both from the sample start),
+// and the first row of the sample that sees the segment.
+struct DqTile {
+    const uint16_t *kb, *vb;
+    int key0, nk;
+    bool causal;
+    int min_row;
+};
+
+// One step (cpattn_step_bwd's dq launch): the sample's rows and keys of the
+// step's mode, one segment.
+struct DqStepPlan {
+    const uint16_t *kb, *vb;
+    int qrow0, nq, nk, ntiles;
+    bool causal;
+    __device__ __forceinline__ void init(const BwdParams &p, int smp, int q0, int n, int g) {
+        const Geo G = geo_of(p, smp, p.mode);
+        qrow0 = G.qrow0;
+        nq = G.nq;
+        nk = G.nk;
+        causal = G.causal;
+        kb = p.k + (((int64_t)n * p.two_c + G.kv0) * p.hkv + g) * D;
+        vb = p.v + (((int64_t)n * p.two_c + G.kv0) * p.hkv + g) * D;
+        const int kend = causal ? min(nk, q0 + TR * NWB) : nk;
+        ntiles = (kend + TR - 1) / TR;
+    }
+    __device__ __forceinline__ DqTile tile(int t) const {
+        return DqTile{kb, vb, min(t, ntiles - 1) * TR, nk, causal, 0};
+    }
+    __device__ __forceinline__ bool comp(int t, int wrow0) const {
+        return causal ? t < min(ntiles, (wrow0 + TR - 1) / TR + 1) : t < ntiles;
+    }
+};
+
+// A rank's whole share for one query tile (the dq of all cp steps in one
+// grid): the sample's 2c local rows, and in streaming order the key
+// segments of its steps -- steps 1 .. r (kv_first_half: keys [0, c) of the
+// blocks of ranks r-1 .. 0), steps r+1 .. cp-1 (q_second_half: keys
+// [0, 2c) of ranks cp-1 .. r+1, seen by rows c .. 2c-1 only; streamed only
+// when the tile has such rows), then step 0 (the rank's own block,
+// causal).  dQ of every step sums in the same accumulator.
+struct DqSharePlan {
+    const uint16_t *k0, *v0;
+    int64_t block;
+    int r, cp, c, cA, cB, nAB, ta, tb, kend, ntiles;
+    int qrow0, nq;
+    bool causal;   // unused: masks come per tile
+    __device__ __forceinline__ void init(const BwdParams &p, int smp, int q0, int n, int g) {
+        const int l0 = p.tab.lcu[smp];
+        c = (p.tab.lcu[smp + 1] - l0) >> 1;
+        qrow0 = l0;
+        nq = 2 * c;
+        k0 = p.k + (((int64_t)n * p.two_c + l0) * p.hkv + g) * D;
+        v0 = p.v + (((int64_t)n * p.two_c + l0) * p.hkv + g) * D;
+        block = p.block_elems;
+        r = p.rank;
+        cp = p.cp;
+        cA = (c + TR - 1) / TR;
+        cB = (2 * c + TR - 1) / TR;
+        nAB = (q0 + TR * NWB > c) ? cp - 1 - r : 0;
+        ta = r * cA;
+        tb = ta + nAB * cB;
+        kend = min(2 * c, q0 + TR * NWB);
+        ntiles = tb + (kend + TR - 1) / TR;
+        causal = false;
+    }
+    __device__ __forceinline__ DqTile tile(int u) const {
+        u = min(u, ntiles - 1);
+        if (u < ta) {
+            const int seg = u / cA;
+            const int64_t off = (int64_t)(r - 1 - seg) * block;
+            return DqTile{k0 + off, v0 + off, (u - seg * cA) * TR, c, false, 0};
+        }
+        if (u < tb) {
+            const int seg = (u - ta) / cB;
+            const int64_t off = (int64_t)(cp - 1 - seg) * block;
+            return DqTile{k0 + off, v0 + off, (u - ta - seg * cB) * TR, 2 * c, false, c};
+        }
+        const int64_t off = (int64_t)r * block;
+        return DqTile{k0 + off, v0 + off, (u - tb) * TR, kend, true, 0};
+    }
+    __device__ __forceinline__ bool comp(int t, int wrow0) const {
+        if (t < ta) return true;
+        if (t < tb) return wrow0 + TR - 1 >= c;
+        return t - tb < min(ntiles - tb, (wrow0 + TR - 1) / TR + 1);
+    }
+};
+
+template <class Plan, bool ACCUMULATE>
+__device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
@@ -207,13 +301,12 @@ attn_bwd_dq(BwdParams p) {
     const int n = item / p.hkv;
     const int head = g * p.group + hh;
     const int smp = seq_of(p.tab.tile0, p.tab.nseq, qt_all);
-    const Geo G = geo_of(p, smp, p.mode);
     const int qt = qt_all - p.tab.tile0[smp];
     const int q0 = qt * TR * NWB;
     const int wrow0 = q0 + wave * TR;
-    const int kend = G.causal ? min(G.nk, q0 + TR * NWB) : G.nk;
-    const int ntiles = (kend + TR - 1) / TR;
-    const int wtiles = G.causal ? min(ntiles, (wrow0 + TR - 1) / TR + 1) : ntiles;
+    Plan P;
+    P.init(p, smp, q0, n, g);
+    const int ntiles = P.ntiles;
 
     LaneOffsets L;
     L.init(lane);
@@ -221,12 +314,12 @@ attn_bwd_dq(BwdParams p) {
 
     // this lane's query row: Q and dO as B operands, L (log2) and D
     const int qrow = wrow0 + l32;
-    const int qr = min(qrow, G.nq - 1);
-    const int64_t qoff = ((n * p.two_c + G.qrow0 + qr) * (int64_t)p.hq + head) * D;
+    const int qr = min(qrow, P.nq - 1);
+    const int64_t qoff = ((n * p.two_c + P.qrow0 + qr) * (int64_t)p.hq + head) * D;
     bf16x8 qf[D / 16], df[D / 16];
     load_b_rows(p.q + qoff, hi, qf);
     load_b_rows(p.dout + qoff, hi, df);
-    const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + G.qrow0 + qr;
+    const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + P.qrow0 + qr;
     const float lq = p.lse[lrow] * LOG2E;
     const float dq_d = p.delta[lrow];
     settle(qf);
@@ -239,18 +332,16 @@ attn_bwd_dq(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
 
-    const uint16_t *kb = p.k + (((int64_t)n * p.two_c + G.kv0) * p.hkv + g) * D;
-    const uint16_t *vb = p.v + (((int64_t)n * p.two_c + G.kv0) * p.hkv + g) * D;
     const int64_t row_bytes = (int64_t)p.hkv * D * 2;
     const unsigned coff = copy_offset(lane, wave, row_bytes);   // m = wave, wave + 4
     // tiles past the last repeat it, so every wave issues 4 copies per tile
     auto issue = [&](int t, int stage) {
-        const int key0 = min(t, ntiles - 1) * TR;
+        const DqTile T = P.tile(t);
         const unsigned sb = lbase + stage * STAGE_DQ;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            copy_rows(kb, row_bytes, key0, G.nk, wave + 4 * i, coff, sb, lane);
-            copy_rows(vb, row_bytes, key0, G.nk, wave + 4 * i, coff, sb + TB, lane);
+            copy_rows(T.kb, row_bytes, T.key0, T.nk, wave + 4 * i, coff, sb, lane);
+            copy_rows(T.vb, row_bytes, T.key0, T.nk, wave + 4 * i, coff, sb + TB, lane);
         }
     };
     if (ntiles > 0) {
@@ -264,7 +355,8 @@ attn_bwd_dq(BwdParams p) {
         int ns = stage + PDQ;
         if (ns >= NSQ) ns -= NSQ;
         issue(t + PDQ, ns);
-        if (t < wtiles) {
+        if (P.comp(t, wrow0)) {
+            const DqTile T = P.tile(t);
             const unsigned sK = lbase + stage * STAGE_DQ, sV = sK + TB;
             // the tile's LDS operands are read ahead of the products
             // (the transposed K^T reads go out behind the S, dP products)
@@ -289,9 +381,10 @@ attn_bwd_dq(BwdParams p) {
                     at[kc][dt] = vt_read2(sK + L.toff(dt, 0) + kc * 16 * RB,
                                           sK + L.toff(dt, 1) + kc * 16 * RB);
             __builtin_amdgcn_sched_barrier(0);
-            const int key0 = t * TR;
+            const int key0 = T.key0;
             // tile entirely visible to the wave's rows: no mask
-            const bool full = key0 + TR <= G.nk && (!G.causal || key0 + TR - 1 <= wrow0);
+            const bool full = key0 + TR <= T.nk && (!T.causal || key0 + TR - 1 <= wrow0) &&
+                              wrow0 >= T.min_row;
             bf16x8 dsb[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
@@ -302,7 +395,8 @@ attn_bwd_dq(BwdParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int key = key0 + 16 * kc + 8 * hi + e;
-                        const bool vis = key < G.nk && (!G.causal || key <= qrow);
+                        const bool vis = key < T.nk && (!T.causal || key <= qrow) &&
+                                         qrow >= T.min_row;
                         x[e] = vis ? x[e] : -INFINITY;
                     }
                 }
@@ -325,20 +419,35 @@ attn_bwd_dq(BwdParams p) {
     }
     wait_vmcnt<0>();
 
-    // dq[row] += scale * dQ: lane holds head dims dt*32 + 8*i + 4*hi + j
-    if (qrow < G.nq) {
+    // dq[row] (+)= scale * dQ: lane holds head dims dt*32 + 8*i + 4*hi + j
+    if (qrow < P.nq) {
         float *dst = p.dq + qoff + 4 * hi;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 f32x4 *a = (f32x4 *)(dst + dt * 32 + i * 8);
-                f32x4 w = *a;
+                f32x4 w = ACCUMULATE ? *a : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) w[j] += p.scale * acc[dt][i * 4 + j];
                 *a = w;
             }
     }
+}
+
+// One step's dq (accumulated into dq).
+__global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
+    dq_body<DqStepPlan, true>(p, lds);
+}
+
+// The dq of all cp steps of a rank's share in one grid: a workgroup streams
+// every step's keys for its query tile and writes dq once.
+__global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_share(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
+    dq_body<DqSharePlan, false>(p, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -727,6 +836,22 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
         p.head_splits *= 2;
     hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)(base_wgs * p.head_splits)),
                        dim3(64 * NWK), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_share_bf16(const StepGeom &g, const SeqTable &tab, int rank, int cp,
+                                    const void *q, const void *kz, const void *vz,
+                                    const void *dout, const float *lse, const float *delta,
+                                    float *dq, hipStream_t stream) {
+    BwdParams p = make_params(g, tab, CPATTN_CAUSAL, q, kz, vz, dout, lse, delta, dq, nullptr,
+                              nullptr);
+    p.rank = rank;
+    p.cp = cp;
+    p.block_elems = g.b * g.two_c * g.hkv * D;
+    // query tiles of the 2c local rows of every sample
+    const int64_t nqt = fill_tiles(p, tab, CPATTN_CAUSAL, false);
+    hipLaunchKernelGGL(attn_bwd_dq_share, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * NWB), 0,
+                       stream, p);
     return hipGetLastError();
 }
 

@@ -81,6 +81,12 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
                                 const void *q, const void *k, const void *v, const void *dout,
                                 const float *lse, const float *delta, float *dq, float *dk,
                                 float *dv, hipStream_t stream, bool with_dkdv = true);
+// The dq of all cp steps of rank's share in one grid (bf16): kz, vz are the
+// partitioned K, V of all ranks; every row of dq is written (not added to).
+hipError_t launch_bwd_dq_share_bf16(const StepGeom &g, const SeqTable &tab, int rank, int cp,
+                                    const void *q, const void *kz, const void *vz,
+                                    const void *dout, const float *lse, const float *delta,
+                                    float *dq, hipStream_t stream);
 // The dK/dV of steps 0 .. n-1 of one rank's share in one grid: step i
 // reads k[i]/v[i] and adds to dk[i]/dv[i] (distinct blocks, zeroed by the
 // caller), mode[i] its mode; g[0] supplies the dims and scale, tab the

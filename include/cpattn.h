@@ -247,10 +247,12 @@ int cpattn_step_bwd(const cpattn_dims *dims, int dtype, float scale, int mode,
                     const void *do_r, const float *lse_r, const float *delta_r,
                     float *dq_r, float *dk_src, float *dv_src, void *stream);
 
-/* cpattn_backward, device: one rank's whole backward share.  Zeroes dq_r
- * [b, 2c, hq, d], dkz and dvz [cp, b, 2c, hkv, d] (fp32), computes delta
- * into delta_ws [b, hq, 2c] (caller's workspace), then the cp steps of
- * cpattn_step_mode; step i adds to rank src's slices of dkz/dvz.  dkz/dvz
+/* cpattn_backward, device: one rank's whole backward share.  Zeroes dkz
+ * and dvz [cp, b, 2c, hkv, d] (fp32), computes delta into delta_ws
+ * [b, hq, 2c] (caller's workspace), then the cp steps of cpattn_step_mode:
+ * dq_r [b, 2c, hq, d] (fp32) is written with the sum over all steps (every
+ * row; its previous contents are ignored), and step i adds to rank src's
+ * slices of dkz/dvz.  dkz/dvz
  * hold the rank's contributions to every rank's K/V gradient: the inputs
  * of the reduce-scatter that sums them on their owners.  qz, kz, vz:
  * partitioned [cp, b, 2c, h, d] bf16; o_r, lse_r: the rank's merged forward

@@ -93,15 +93,36 @@ __global__ void __launch_bounds__(NT) partition_copy(CopyParams p) {
         }
     }
     __syncthreads();
+    // Eight 16-byte reads in flight per lane before the eight writes: one
+    // read at a time (a write between them) leaves HBM latency-bound.
+    // Full blocks run unpredicated; the last block one vector at a time.
+    constexpr int U = 8;
     const int nvec = p.rows_per_block * p.vecs_per_row;
-    for (int i = threadIdx.x; i < nvec; i += NT) {
+    const int64_t rows_here = p.rows_total - row0;
+    const int full = rows_here >= p.rows_per_block ? nvec / (U * NT) * (U * NT) : 0;
+    const __attribute__((address_space(1))) u32x4 *xg =
+        (const __attribute__((address_space(1))) u32x4 *)p.x;
+    __attribute__((address_space(1))) u32x4 *zg = (__attribute__((address_space(1))) u32x4 *)p.xz;
+    for (int i0 = 0; i0 < full; i0 += U * NT) {
+        u32x4 v[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int i = i0 + k * NT + threadIdx.x;
+            const int rr = i / p.vecs_per_row;
+            v[k] = xg[srow[rr] * p.vecs_per_row + (i - rr * p.vecs_per_row)];
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int i = i0 + k * NT + threadIdx.x;
+            zg[row0 * p.vecs_per_row + i] = v[k];
+        }
+    }
+    for (int i = full + threadIdx.x; i < nvec; i += NT) {
         const int rr = i / p.vecs_per_row;
         const int vv = i - rr * p.vecs_per_row;
         const int64_t row = row0 + rr;
         if (row >= p.rows_total) break;
-        const u32x4 *src = (const u32x4 *)p.x + srow[rr] * p.vecs_per_row + vv;
-        u32x4 *dst = (u32x4 *)p.xz + row * p.vecs_per_row + vv;
-        *dst = *src;
+        zg[row * p.vecs_per_row + vv] = xg[srow[rr] * p.vecs_per_row + vv];
     }
     if (p.pos != nullptr && blockIdx.x == 0) write_positions(p.tab, p.cp, p.tloc, p.pos);
 }

@@ -161,7 +161,7 @@ def share_step_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(collectives are out of scope); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np

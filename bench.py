@@ -158,6 +158,40 @@ def share_step_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
     return flops / (steps * 1e-3) / 1e12, flops / (whole * 1e-3) / 1e12
 
 
+def peak_check(C, torch, stream, iters=10000, rounds=4):
+    """The bf16 MFMA rate this part sustains on a pure matrix stream (random
+    operands, two waves per SIMD, one workgroup per CU at a time, 'rounds'
+    workgroups per CU), beside the published peak; plus the device's
+    compute units and maximum clock."""
+    import numpy as np
+    cus, khz = C.cpattn_device_info()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    ops = (torch.randn(4096, generator=gen, device="cuda") * 0.5).to(torch.bfloat16)
+    blocks = cus * rounds
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    flops = blocks * 8 * iters * 16 * 32768
+    with torch.cuda.stream(stream):
+        C.cpattn_probe_mfma(ops, out, blocks, iters, stream)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(3):
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record(stream)
+            C.cpattn_probe_mfma(ops, out, blocks, iters, stream)
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+    return {"compute_units": cus, "max_clock_mhz": khz / 1000.0,
+            "published_peak_tflops": PEAK_BF16_TFLOPS,
+            "peak_at_max_clock_tflops": round(cus * 4 * 1024 * khz * 1e3 / 1e12, 1),
+            "mfma_probe_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "probe": "v_mfma_f32_32x32x16_bf16 stream, random bf16 operands, "
+                     f"2 waves per SIMD, one workgroup per CU at a time, {rounds} rounds "
+                     "(cpattn_probe_mfma)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -440,6 +474,10 @@ def main():
             del Pc
             torch.cuda.empty_cache()
         line["configs"] = configs
+    if w.dtype == "bf16":
+        pc = peak_check(C, torch, stream)
+        pc["achieved_over_probe"] = round(attn_tflops / pc["mfma_probe_tflops"], 4)
+        line["peak_check"] = pc
     if args.cpu_sample_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, rank, args.cpu_sample_seconds)
     else:

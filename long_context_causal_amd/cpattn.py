@@ -97,6 +97,8 @@ def lib():
         L.cpattn_bwd_delta.argtypes = [D, P, P, P, P]
         L.cpattn_step_bwd.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P]
         L.cpattn_backward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P, P]
+        L.cpattn_probe_mfma.argtypes = [P, P, I, I, P]
+        L.cpattn_device_info.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I)]
         L.cpattn_status_str.argtypes = [I]
         L.cpattn_status_str.restype = ctypes.c_char_p
         for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
@@ -104,7 +106,7 @@ def lib():
                      "cpattn_forward_fused", "cpattn_bwd_delta", "cpattn_step_bwd",
                      "cpattn_backward", "cpattn_partition_positions_varlen",
                      "cpattn_partition_varlen", "cpattn_forward_fused_varlen",
-                     "cpattn_backward_varlen"):
+                     "cpattn_backward_varlen", "cpattn_probe_mfma", "cpattn_device_info"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -268,3 +270,20 @@ def cpattn_backward_varlen(dims, dtype, scale, rank, cu_seqlens, qz, kz, vz, o_r
                                         _ptr(dq_r), _ptr(dkz), _ptr(dvz), _stream(stream)),
            "cpattn_backward_varlen")
     del keep
+
+
+# --- measurement helpers (include/cpattn_probe.h) -------------------------------
+
+def cpattn_probe_mfma(operands, out, blocks, iters, stream=None):
+    """Pure-MFMA rate probe: blocks * 8 * iters * 16 * 32768 FLOP."""
+    if lib().cpattn_probe_mfma(_ptr(operands), _ptr(out), int(blocks), int(iters),
+                               _stream(stream)) != 0:
+        raise RuntimeError("cpattn_probe_mfma failed")
+
+
+def cpattn_device_info():
+    """(compute units, maximum engine clock in kHz) of the current device."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    if lib().cpattn_device_info(ctypes.byref(cus), ctypes.byref(khz)) != 0:
+        raise RuntimeError("cpattn_device_info failed")
+    return cus.value, khz.value

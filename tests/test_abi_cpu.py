@@ -22,8 +22,11 @@ def built_library():
 
 
 def _declared_functions():
-    with open(os.path.join(ROOT, "include", "cpattn.h")) as f:
-        text = f.read()
+    text = ""
+    for name in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if name.endswith(".h"):
+            with open(os.path.join(ROOT, "include", name)) as f:
+                text += f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(cpattn_\w+)\s*\(", text)))
 

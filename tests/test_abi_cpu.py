@@ -312,3 +312,12 @@ def test_backward_varlen_validates_before_launch():
     args[5] = ALIGNED + 8
     assert L.cpattn_backward_varlen(*args) == C.CPATTN_EALIGN
     del keep, keep2
+
+
+def test_probe_validation_before_launch():
+    L = C.lib()
+    assert L.cpattn_probe_mfma(None, ALIGNED, 1, 1, None) == 1
+    assert L.cpattn_probe_mfma(ALIGNED + 8, ALIGNED, 1, 1, None) == 1   # 16-byte alignment
+    assert L.cpattn_probe_mfma(ALIGNED, ALIGNED, 0, 1, None) == 1
+    assert L.cpattn_probe_mfma(ALIGNED, ALIGNED, 1, 0, None) == 1
+    assert L.cpattn_device_info(None, None) == 1

@@ -243,9 +243,8 @@ def test_backward_varlen_one_sample_is_unpacked():
     P.backward(g, out["o"], out["lse"], do_r)
     Pv.backward(gv, out["o"], out["lse"], do_r)
     torch.cuda.synchronize()
-    # dq is written by one workgroup per row; dK/dV add with atomics whose
-    # order may differ, so they agree to fp32 rounding
-    assert torch.equal(g["dq"], gv["dq"])
-    for key in ("dkz", "dvz"):
-        np.testing.assert_allclose(gv[key].cpu().numpy(), g[key].cpu().numpy(), rtol=1e-5,
-                                   atol=1e-6)
+    # dq is written by one workgroup per row, and every dK/dV element by one
+    # workgroup of the share's grid: the one-sample table is the unpacked
+    # call, bit for bit
+    for key in ("dq", "dkz", "dvz"):
+        assert torch.equal(g[key], gv[key]), key

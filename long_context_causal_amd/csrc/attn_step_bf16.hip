@@ -141,7 +141,7 @@ struct StepPlan {
     // whether the wave whose rows start at wrow0 computes tile t: causal
     // waves stop after their diagonal
     __device__ __forceinline__ bool comp(int t, int wrow0) const {
-        if (t < 0) return false;
+        if (t < 0 || wrow0 >= nq) return false;   // a wave past the last row idles
         return CAUSAL ? t < min(ntiles, (wrow0 + 31) / BN + 1) : t < ntiles;
     }
 };
@@ -199,7 +199,7 @@ struct FusedPlan {
         return TileRef{k0 + off, v0 + off, (u - tb) * BN, kend, true, 0};
     }
     __device__ __forceinline__ bool comp(int t, int wrow0) const {
-        if (t < 0) return false;
+        if (t < 0 || wrow0 >= nq) return false;   // a wave past the sample's rows idles
         if (t < ta) return true;
         if (t < tb) return wrow0 + 31 >= c;
         return t - tb < min(ntiles - tb, (wrow0 + 31) / BN + 1);

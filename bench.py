@@ -240,6 +240,24 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
+    # the HBM kernels alone with the 256 MB last-level cache evicted first:
+    # a 512 MB scratch write between repetitions, outside the timed region
+    cold = {"partition": [], "merge": []}
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    with torch.cuda.stream(stream):
+        for _ in range(max(args.steps // 2, 3)):
+            for name, fn in (("partition", lambda: P.partition(stream)),
+                             ("merge", lambda: P.merge(buf, stream))):
+                scratch.fill_(1)
+                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                cold[name].append((e0, e1))
+        torch.cuda.synchronize()
+    del scratch
+    cold_ms = {k: float(np.median([a.elapsed_time(b) for a, b in v])) for k, v in cold.items()}
+
     # the same steps launched one by one (cpattn_step_fwd), each timed
     per_step = None
     with torch.cuda.stream(stream):
@@ -412,6 +430,10 @@ def main():
         "steps_plus_merge_tflops": round(flops / ((attn_ms + mean(merge_ms)) * 1e-3) / 1e12, 2),
         "partition_gbps": round(part_bytes / (mean(part_ms) * 1e-3) / 1e9, 1),
         "merge_gbps": round(merge_bytes / (mean(merge_ms) * 1e-3) / 1e9, 1),
+        "cold_cache_gbps": {"partition": round(part_bytes / (cold_ms["partition"] * 1e-3) / 1e9, 1),
+                            "merge": round(merge_bytes / (cold_ms["merge"] * 1e-3) / 1e9, 1),
+                            "note": "each launch after a 512 MB scratch write (last-level "
+                                    "cache evicted), median"},
         "rank_flops": flops,
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
     }

@@ -221,6 +221,7 @@ struct DqStepPlan {
         return DqTile{kb, vb, min(t, ntiles - 1) * TR, nk, causal, 0};
     }
     __device__ __forceinline__ bool comp(int t, int wrow0) const {
+        if (wrow0 >= nq) return false;   // a wave past the last row idles
         return causal ? t < min(ntiles, (wrow0 + TR - 1) / TR + 1) : t < ntiles;
     }
 };
@@ -273,6 +274,7 @@ struct DqSharePlan {
         return DqTile{k0 + off, v0 + off, (u - tb) * TR, kend, true, 0};
     }
     __device__ __forceinline__ bool comp(int t, int wrow0) const {
+        if (wrow0 >= nq) return false;   // a wave past the sample's rows idles
         if (t < ta) return true;
         if (t < tb) return wrow0 + TR - 1 >= c;
         return t - tb < min(ntiles - tb, (wrow0 + TR - 1) / TR + 1);
@@ -566,7 +568,8 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
         issue(it + PDK, ns);
         const int u = ds_wave ? it - 1 : it;
         const int q0 = (qstart + (u < 0 ? 0 : u) % per_head) * TR;
-        if (u >= 0 && u < ntiles && (!G.causal || q0 + TR - 1 >= wkey0)) {
+        // (a key group past the last key idles)
+        if (u >= 0 && u < ntiles && wkey0 < G.nk && (!G.causal || q0 + TR - 1 >= wkey0)) {
             const unsigned sT = lbase + (ds_wave ? st_ds : st_p) * STAGE_DKDV;
             const unsigned lslot = sT + 2 * TB + wave * LD_SLOT;
             const unsigned slab = slab0 + (u & 1) * (KW * PSLAB);

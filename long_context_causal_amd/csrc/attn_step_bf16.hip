@@ -503,11 +503,13 @@ struct Kernel {
 
         // Half-iterations h = 0 .. 2T+1, one barrier each.  The leading group
         // runs phase h, the trailing group phase h-1: phase 2t is the matrix
-        // phase G(t), phase 2t+1 the softmax of tile t.  At even h = 2u tile u
-        // must be resident (its K is read now, its V two phases later) and
-        // tile u+2 is copied into the stage tile u-2 left (its last reader ran
-        // at h-1).  The trailing group's first and the leading group's last
-        // half-iteration are idle.
+        // phase G(t), phase 2t+1 the softmax of tile t.  Tile u is resident
+        // from barrier 2u-1 on (its K is read ahead in phase 2u-1 by the
+        // leading group, its V two phases after its K), and after barrier 2u
+        // tile u+2 is copied into the stage tile u-2 left (its last readers,
+        // the matrix phases of tile u-1 and the reads ahead of them, ran
+        // before that barrier).  The trailing group's first and the leading
+        // group's last half-iteration are idle.
         // A wave computes tile t when P.comp(t): the matrix phase G(t) runs
         // when it needs S(t) or adds P(t-1); after a tile the wave skips, P is
         // zero, so a following G adds nothing for it.

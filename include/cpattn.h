@@ -55,8 +55,9 @@ typedef struct cpattn_dims {
     int64_t s;    /* full sequence length, a multiple of 2*cp                 */
     int32_t hq;   /* query heads, a multiple of hkv                           */
     int32_t hkv;  /* key/value heads (GQA groups)                              */
-    int32_t d;    /* head dimension: 64 or 128                                 */
-    int32_t cp;   /* context-parallel size (ranks emulated), 1..64             */
+    int32_t d;    /* head dimension: 128 (every path); 64 (the fp32 path only) */
+    int32_t cp;   /* context-parallel size (ranks emulated), >= 1: any cp with
+                     s % (2*cp) == 0, down to chunks of one row (c = 1)       */
 } cpattn_dims;
 
 /* Element types of Q, K, V (and of the merged output). */
@@ -73,7 +74,9 @@ enum {
 enum {
     CPATTN_OK = 0,
     CPATTN_EINVAL = 1,   /* null pointer, bad enum, rank/step out of range   */
-    CPATTN_ESHAPE = 2,   /* s % 2cp, hq % hkv, unsupported d, b or s < 1     */
+    CPATTN_ESHAPE = 2,   /* s % 2cp, hq % hkv, unsupported d, b or s < 1, or
+                            a launch that would need more than 2^31-1
+                            workgroups                                       */
     CPATTN_EDTYPE = 3,   /* dtype not supported by this entry point          */
     CPATTN_EALIGN = 4,   /* a device pointer is not 16-byte aligned          */
     CPATTN_ENOSPACE = 5, /* workspace too small                              */
@@ -115,8 +118,8 @@ typedef struct cpattn_varlen {
 
 #define CPATTN_MAX_SEQS 128
 
-#define CPATTN_MAX_PARTIALS 64
-#define CPATTN_MAX_MERGE_WEIGHTS 8192   /* hq * n per merge call */
+/* Partials one merge pass folds (cpattn_merge). */
+#define CPATTN_MERGE_PASS 64
 
 /* Mode and KV source of a step, host only, pure.
  * "Megatron-LM 篇" 3.4: step 0 is causal; steps 1..rank drop the second
@@ -156,7 +159,7 @@ int cpattn_partition(const cpattn_dims *dims, int dtype, int h, const void *x,
  * CPATTN_KV_FIRST_HALF or CPATTN_Q_SECOND_HALF.
  * Writes o [b, rows, hq, d] fp32 (normalised within the step) and
  * lse [b, hq, rows] fp32, rows = 2c (first two modes) or c (the last one,
- * holding local rows c..2c-1).  d: 64 or 128. */
+ * holding local rows c..2c-1).  ESHAPE for any other d. */
 int cpattn_step_fwd(const cpattn_dims *dims, int dtype, float scale, int mode,
                     const void *q_r, const void *k_src, const void *v_src,
                     float *o, float *lse, void *stream);
@@ -165,16 +168,34 @@ int cpattn_step_fwd(const cpattn_dims *dims, int dtype, float scale, int mode,
  * 5), device.  For each batch n, local row j in [0, 2c) and head h, over the
  * partials that cover j: M = max L_p, L = M + ln sum_p exp(L_p - M),
  * O = sum_p exp(L_p - L) O_p.  A row no partial covers gets L = -inf, O = 0.
- * p: host array of n descriptors (device pointers inside), 1 <= n <=
- * CPATTN_MAX_PARTIALS and hq * n <= CPATTN_MAX_MERGE_WEIGHTS (ESHAPE
- * otherwise); each partial's rows must lie inside [0, 2c).  out_dtype: CPATTN_F32 or CPATTN_BF16 (round to
- * nearest even).  o_out [b, 2c, hq, d]; lse_out [b, hq, 2c] fp32 or NULL. */
+ * p: host array of n >= 1 descriptors (device pointers inside), read during
+ * the call only; each partial's rows must lie inside [0, 2c) (ESHAPE
+ * otherwise).  out_dtype: CPATTN_F32 or CPATTN_BF16 (round to nearest
+ * even).  o_out [b, 2c, hq, d]; lse_out [b, hq, 2c] fp32 or NULL.
+ * One launch folds up to CPATTN_MERGE_PASS partials; a longer merge runs in
+ * passes that carry the running result in o_out and lse_out, so for
+ * n > CPATTN_MERGE_PASS out_dtype must be CPATTN_F32 and lse_out non-NULL
+ * (ESHAPE otherwise; cpattn_forward has no such limit). */
 int cpattn_merge(const cpattn_dims *dims, int n, const cpattn_partial *p,
                  int out_dtype, void *o_out, float *lse_out, void *stream);
 
-/* Bytes of device workspace cpattn_forward needs for 'rank' (the fp32
- * partials of all cp steps).  Returns 0 on invalid dims or rank. */
+/* Bytes of device workspace cpattn_forward needs for 'rank': the fp32
+ * partials of all cp steps, plus, when cp > CPATTN_MERGE_PASS, one fp32 O
+ * and L of the rank's 2c rows for the running result of the merge passes.
+ * Returns 0 on invalid dims or rank. */
 size_t cpattn_forward_workspace(const cpattn_dims *dims, int rank);
+
+/* Where cpattn_forward_steps puts each step's partial inside a workspace,
+ * host only, pure: parts[i] (i = step, caller-owned host array of cp
+ * entries) receives the device addresses of step i's O_i [b, rows, hq, d]
+ * and L_i [b, hq, rows] inside ws and the local rows they cover: row0 = 0,
+ * rows = 2c for the causal and kv_first_half steps; row0 = c, rows = c
+ * for the q_second_half steps (cpattn_step_mode gives the modes).  The
+ * descriptors are what cpattn_merge takes.  EINVAL for a NULL pointer or a
+ * rank out of range, ESHAPE for bad dims, EALIGN unless ws is 256-byte
+ * aligned, ENOSPACE if ws_bytes < cpattn_forward_workspace. */
+int cpattn_forward_partials(const cpattn_dims *dims, int rank, void *ws, size_t ws_bytes,
+                            cpattn_partial *parts);
 
 /* The cp steps of one rank's forward share ("Megatron-LM 篇" 3.2 step 2,
  * the steps of cpattn_step_mode), device, without the merge: step i reads
@@ -270,7 +291,7 @@ int cpattn_backward(const cpattn_dims *dims, int dtype, float scale, int rank,
  * cpattn_partition_positions_varlen, host, pure: the in-sample positions
  * of rank 'rank''s s/cp local rows into pos (caller-owned host array of
  * s/cp int32).  EINVAL for a NULL pos or offset array or a rank out of
- * range, ESHAPE for bad offsets or cp > CPATTN_MAX_PARTIALS. */
+ * range, ESHAPE for bad offsets. */
 int cpattn_partition_positions_varlen(int64_t s, int cp, int rank, const cpattn_varlen *vl,
                                       int32_t *pos);
 

@@ -22,7 +22,7 @@ CPATTN_KV_FIRST_HALF = 1
 CPATTN_Q_SECOND_HALF = 2
 CPATTN_OK, CPATTN_EINVAL, CPATTN_ESHAPE, CPATTN_EDTYPE, CPATTN_EALIGN, \
     CPATTN_ENOSPACE, CPATTN_EHIP = range(7)
-CPATTN_MAX_PARTIALS = 64
+CPATTN_MERGE_PASS = 64
 CPATTN_MAX_SEQS = 128
 
 
@@ -81,6 +81,8 @@ def lib():
         L.cpattn_merge.argtypes = [D, I, ctypes.POINTER(cpattn_partial), I, P, P, P]
         L.cpattn_forward_workspace.argtypes = [D, I]
         L.cpattn_forward_workspace.restype = ctypes.c_size_t
+        L.cpattn_forward_partials.argtypes = [D, I, P, ctypes.c_size_t,
+                                              ctypes.POINTER(cpattn_partial)]
         L.cpattn_forward_steps.argtypes = [D, I, ctypes.c_float, I, P, P, P, P,
                                            ctypes.c_size_t, P]
         L.cpattn_forward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, ctypes.c_size_t,
@@ -102,7 +104,8 @@ def lib():
         L.cpattn_status_str.argtypes = [I]
         L.cpattn_status_str.restype = ctypes.c_char_p
         for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
-                     "cpattn_step_fwd", "cpattn_merge", "cpattn_forward_steps", "cpattn_forward",
+                     "cpattn_step_fwd", "cpattn_merge", "cpattn_forward_partials",
+                     "cpattn_forward_steps", "cpattn_forward",
                      "cpattn_forward_fused", "cpattn_bwd_delta", "cpattn_step_bwd",
                      "cpattn_backward", "cpattn_partition_positions_varlen",
                      "cpattn_partition_varlen", "cpattn_forward_fused_varlen",
@@ -182,6 +185,15 @@ def cpattn_merge(dims, partials, out_dtype, o_out, lse_out=None, stream=None):
 
 def cpattn_forward_workspace(dims, rank):
     return int(lib().cpattn_forward_workspace(ctypes.byref(dims), rank))
+
+
+def cpattn_forward_partials(dims, rank, ws, ws_bytes):
+    """The step partials inside a workspace: a list of (o address, lse
+    address, row0, rows), one per step."""
+    arr = (cpattn_partial * dims.cp)()
+    _check(lib().cpattn_forward_partials(ctypes.byref(dims), rank, _ptr(ws), int(ws_bytes), arr),
+           "cpattn_forward_partials")
+    return [(p.o, p.lse, p.row0, p.rows) for p in arr]
 
 
 def cpattn_forward_steps(dims, dtype, scale, rank, qz, kz, vz, ws, ws_bytes, stream=None):

@@ -44,6 +44,8 @@
 
 #include <math.h>
 
+#include <vector>
+
 namespace cpattn {
 namespace {
 
@@ -866,7 +868,7 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &
     // longest workgroups first: kv_first_half key tiles (every query row),
     // q_second_half tiles (the second chunk's rows), then the causal step
     // (its first key tiles see the most rows)
-    int order[CPATTN_MAX_PARTIALS];
+    std::vector<int> order(n);
     int m = 0;
     for (int pass = 0; pass < 3; ++pass)
         for (int i = 0; i < n; ++i) {

@@ -688,49 +688,46 @@ hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, con
 hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void *const *k,
                              const void *const *v, float *const *o, float *const *lse,
                              hipStream_t stream) {
+    static_assert(MAX_STEPS == STEPS_PER_GRID, "one grid takes the steps of one call");
+    if (n < 1 || n > MAX_STEPS) return hipErrorInvalidValue;
     // longest workgroups first: the steps whose query tiles stream the most
     // key tiles (q_second_half: 2c keys; kv_first_half: c keys), then the
     // causal step, whose own tiles run from its longest to its shortest
-    int order[CPATTN_MAX_PARTIALS];
+    int order[MAX_STEPS];
     int m = 0;
     for (int pass = 0; pass < 3; ++pass)
         for (int i = 0; i < n; ++i) {
             const int cls = g[i].causal ? 2 : (g[i].nk >= g[i].nq ? 0 : 1);
             if (cls == pass) order[m++] = i;
         }
-    for (int j0 = 0; j0 < n; j0 += MAX_STEPS) {
-        const int nb = n - j0 < MAX_STEPS ? n - j0 : MAX_STEPS;
-        StepsParams sp = {};
-        sp.q = (const uint16_t *)q;
-        sp.two_c = g[0].two_c;
-        sp.hq = g[0].hq;
-        sp.hkv = g[0].hkv;
-        sp.group = g[0].hq / g[0].hkv;
-        sp.scale_log2 = g[0].scale_log2;
-        sp.nsteps = nb;
-        int items = 0;
-        for (int jj = 0; jj < nb; ++jj) {
-            const int i = order[j0 + jj];
-            StepDesc &d = sp.st[jj];
-            d.k = (const uint16_t *)k[i];
-            d.v = (const uint16_t *)v[i];
-            d.o = o[i];
-            d.lse = lse[i];
-            d.q_row0 = (int)g[i].q_row0;
-            d.nq = (int)g[i].nq;
-            d.nk = (int)g[i].nk;
-            d.causal = g[i].causal ? 1 : 0;
-            d.num_qtiles = (int)((g[i].nq + BM - 1) / BM);
-            d.item0 = items;
-            items += d.num_qtiles * sp.group;
-        }
-        sp.items = items;
-        const int64_t blocks = (int64_t)items * sp.hkv * g[0].b;
-        hipLaunchKernelGGL(attn_steps_bf16, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, sp);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    StepsParams sp = {};
+    sp.q = (const uint16_t *)q;
+    sp.two_c = g[0].two_c;
+    sp.hq = g[0].hq;
+    sp.hkv = g[0].hkv;
+    sp.group = g[0].hq / g[0].hkv;
+    sp.scale_log2 = g[0].scale_log2;
+    sp.nsteps = n;
+    int items = 0;
+    for (int jj = 0; jj < n; ++jj) {
+        const int i = order[jj];
+        StepDesc &d = sp.st[jj];
+        d.k = (const uint16_t *)k[i];
+        d.v = (const uint16_t *)v[i];
+        d.o = o[i];
+        d.lse = lse[i];
+        d.q_row0 = (int)g[i].q_row0;
+        d.nq = (int)g[i].nq;
+        d.nk = (int)g[i].nk;
+        d.causal = g[i].causal ? 1 : 0;
+        d.num_qtiles = (int)((g[i].nq + BM - 1) / BM);
+        d.item0 = items;
+        items += d.num_qtiles * sp.group;
     }
-    return hipSuccess;
+    sp.items = items;
+    const int64_t blocks = (int64_t)items * sp.hkv * g[0].b;
+    hipLaunchKernelGGL(attn_steps_bf16, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, sp);
+    return hipGetLastError();
 }
 
 hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz, const void *vz,

@@ -3,8 +3,11 @@
 // returns the hipError_t of its launch.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
+#ifdef __HIPCC__
+#include <hip/hip_runtime.h>
+#endif
 
 #include "cpattn.h"
 
@@ -35,8 +38,11 @@ struct SeqTable {
     int32_t tile0[CPATTN_MAX_SEQS + 1];
 };
 
-// Largest i in [0, n) with a[i] <= x (a ascending, a[0] <= x).
-__host__ __device__ inline int seq_of(const int32_t *a, int n, int x) {
+#ifdef __HIPCC__
+// Largest i in [0, n) with a[i] <= x (a ascending, a[0] <= x); device code
+// only (the host side of the library also builds with a plain C++ compiler
+// for its sanitizer tests).
+__device__ inline int seq_of(const int32_t *a, int n, int x) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -44,6 +50,7 @@ __host__ __device__ inline int seq_of(const int32_t *a, int n, int x) {
     }
     return lo;
 }
+#endif
 
 hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const SeqTable &tab,
                             const void *x, void *xz, int32_t *pos,
@@ -53,7 +60,10 @@ hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k,
                             const void *v, float *o, float *lse,
                             hipStream_t stream);
 // Steps 0 .. n-1 of one rank's share (bf16) in one grid: step i reads
-// k[i]/v[i] and writes o[i]/lse[i], as launch_step_bf16 would.
+// k[i]/v[i] and writes o[i]/lse[i], as launch_step_bf16 would.  At most
+// STEPS_PER_GRID steps per call (their descriptors travel in the kernel
+// arguments); hipErrorInvalidValue otherwise.
+constexpr int STEPS_PER_GRID = 32;
 hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void *const *k,
                              const void *const *v, float *const *o, float *const *lse,
                              hipStream_t stream);
@@ -109,11 +119,16 @@ hipError_t launch_step_f32(const StepGeom &g, const void *q, const void *k,
                            const void *v, float *o, float *lse,
                            hipStream_t stream);
 
+// One launch of the merge: n <= CPATTN_MERGE_PASS partials, plus (when
+// run_o is not null) the running fp32 result of earlier passes, folded in as
+// a partial that covers every row; run_o / run_l may alias o_out / lse_out.
 struct MergeArgs {
     int64_t b, two_c;
     int32_t hq, d;
     int n;
     const cpattn_partial *parts;   // host array, n entries
+    const float *run_o;            // [b, 2c, hq, d] fp32, or null
+    const float *run_l;            // [b, hq, 2c] fp32 (with run_o)
     int out_dtype;
     void *o_out;
     float *lse_out;

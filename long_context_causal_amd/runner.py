@@ -71,6 +71,13 @@ class CPProblem:
         C.cpattn_partition(self.dims, self.dtype, self.w.hkv, self.v, self.vz, None,
                            None, stream)
 
+    def partition_one(self, which, stream=None):
+        """The split of one tensor ("q", "k" or "v"; unpacked batches)."""
+        h, x, xz, pos, theta = {"q": (self.w.hq, self.q, self.qz, self.pos, self.w.rope_theta),
+                                "k": (self.w.hkv, self.k, self.kz, None, self.w.rope_theta),
+                                "v": (self.w.hkv, self.v, self.vz, None, None)}[which]
+        C.cpattn_partition(self.dims, self.dtype, h, x, xz, pos, theta, stream)
+
     # --- one rank's share ----------------------------------------------------
     def alloc_rank(self, rank, out_dtype=None):
         """Workspace, step partial views and outputs for ``rank``."""
@@ -82,18 +89,16 @@ class CPProblem:
                         dtype=torch.bfloat16 if out_dtype == C.CPATTN_BF16 else torch.float32,
                         device=self.device)
         lse = torch.empty((self.b, self.w.hq, two_c), dtype=torch.float32, device=self.device)
-        # the same carving cpattn_forward uses: per step O then L, 256-byte rounded
+        # each step's partial where cpattn_forward_steps writes it
         steps = []
-        off = 0
-        for i in range(self.cp):
+        base = ws.data_ptr()
+        parts = C.cpattn_forward_partials(self.dims, rank, ws, ws_bytes)
+        for i, (o_addr, l_addr, row0, rows) in enumerate(parts):
             mode, src = C.cpattn_step_mode(i, rank, self.cp)
-            rows = self.c if mode == C.CPATTN_Q_SECOND_HALF else two_c
-            ob = _round256(self.b * rows * self.w.hq * self.w.d * 4)
-            lb = _round256(self.b * self.w.hq * rows * 4)
-            po = ws[off:off + ob].view(torch.float32)[: self.b * rows * self.w.hq * self.w.d]
-            pl = ws[off + ob:off + ob + lb].view(torch.float32)[: self.b * self.w.hq * rows]
-            off += ob + lb
-            row0 = self.c if mode == C.CPATTN_Q_SECOND_HALF else 0
+            n_o = self.b * rows * self.w.hq * self.w.d
+            n_l = self.b * self.w.hq * rows
+            po = ws[o_addr - base:o_addr - base + 4 * n_o].view(torch.float32)
+            pl = ws[l_addr - base:l_addr - base + 4 * n_l].view(torch.float32)
             steps.append(dict(mode=mode, src=src, rows=rows, row0=row0,
                               o=po.view(self.b, rows, self.w.hq, self.w.d),
                               lse=pl.view(self.b, self.w.hq, rows)))
@@ -166,6 +171,3 @@ class CPProblem:
                           self.vz, o_r, do_r, lse_r, grads["delta"], grads["dq"], grads["dkz"],
                           grads["dvz"], stream)
 
-
-def _round256(x):
-    return (x + 255) // 256 * 256

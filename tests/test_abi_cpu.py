@@ -131,13 +131,15 @@ def test_merge_validation_before_launch():
                                   C.cpattn_partial(ALIGNED, ALIGNED, 128, 128))
     bad_rows = (C.cpattn_partial * 1)(C.cpattn_partial(ALIGNED, ALIGNED, 200, 100))
     assert L.cpattn_merge(ctypes.byref(d), 0, good, 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
-    assert L.cpattn_merge(ctypes.byref(d), 65, good, 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
+    many = (C.cpattn_partial * 65)(*([C.cpattn_partial(ALIGNED, ALIGNED, 0, two_c)] * 65))
+    # more than one pass: the running result needs an fp32 O and an L
+    assert L.cpattn_merge(ctypes.byref(d), 65, many, 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
+    assert L.cpattn_merge(ctypes.byref(d), 65, many, 1, ALIGNED, ALIGNED, 0) == C.CPATTN_ESHAPE
     assert L.cpattn_merge(ctypes.byref(d), 1, bad_rows, 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
     assert L.cpattn_merge(ctypes.byref(d), 2, good, 9, ALIGNED, None, 0) == C.CPATTN_EDTYPE
     assert L.cpattn_merge(ctypes.byref(d), 2, good, 0, None, None, 0) == C.CPATTN_EINVAL
     assert L.cpattn_merge(ctypes.byref(d), 2, good, 0, ALIGNED + 4, None, 0) == C.CPATTN_EALIGN
-    assert L.cpattn_merge(ctypes.byref(_dims(hq=256, hkv=4)), 64,
-                          (C.cpattn_partial * 64)(), 0, ALIGNED, None, 0) == C.CPATTN_ESHAPE
+    assert L.cpattn_merge(ctypes.byref(d), 65, many, 0, ALIGNED, ALIGNED + 2, 0) == C.CPATTN_EALIGN
 
 
 def test_forward_workspace_and_validation():
@@ -158,6 +160,55 @@ def test_forward_workspace_and_validation():
     args[7] = ALIGNED
     args[3] = 8
     assert L.cpattn_forward(*args) == C.CPATTN_EINVAL
+
+
+@pytest.mark.parametrize("cp,rank", [(8, 3), (8, 0), (1, 0), (128, 77), (256, 255)])
+def test_forward_partials_layout(cp, rank):
+    """cpattn_forward_partials: step order, O then L per step, 256-byte
+    regions, the rows of each step's mode; for cp above one merge pass the
+    workspace also holds the running fp32 O and L of the 2c rows."""
+    b, s, hq, hkv, d = 1, 32768, 4, 2, 128
+    dims = _dims(b=b, s=s, hq=hq, hkv=hkv, d=d, cp=cp)
+    c = s // (2 * cp)
+    ws_bytes = C.cpattn_forward_workspace(dims, rank)
+    parts = C.cpattn_forward_partials(dims, rank, ALIGNED, ws_bytes)
+    assert len(parts) == cp
+    r256 = lambda x: (x + 255) // 256 * 256
+    off = 0
+    for i, (o, lse, row0, rows) in enumerate(parts):
+        mode, _ = ocp.step_schedule(i, rank, cp)
+        want_rows = c if mode == ocp.Q_SECOND_HALF else 2 * c
+        assert (row0, rows) == ((c, c) if mode == ocp.Q_SECOND_HALF else (0, 2 * c))
+        assert rows == want_rows
+        assert o == ALIGNED + off
+        off += r256(b * rows * hq * d * 4)
+        assert lse == ALIGNED + off
+        off += r256(b * hq * rows * 4)
+    running = r256(b * 2 * c * hq * d * 4) + r256(b * hq * 2 * c * 4) if cp > 64 else 0
+    assert ws_bytes == off + running
+    with pytest.raises(C.CpattnError) as e:
+        C.cpattn_forward_partials(dims, rank, ALIGNED, ws_bytes - 1)
+    assert e.value.status == C.CPATTN_ENOSPACE
+    with pytest.raises(C.CpattnError) as e:
+        C.cpattn_forward_partials(dims, rank, ALIGNED + 16, ws_bytes)
+    assert e.value.status == C.CPATTN_EALIGN
+    with pytest.raises(C.CpattnError) as e:
+        C.cpattn_forward_partials(dims, cp, ALIGNED, ws_bytes)
+    assert e.value.status == C.CPATTN_EINVAL
+
+
+def test_backward_grids_past_32_bits_rejected():
+    """A share whose backward would need more than 2^31-1 workgroups is
+    refused before any launch (here 2^23 query tiles x 512 heads)."""
+    L = C.lib()
+    d = _dims(b=1, s=1 << 30, hq=512, hkv=512, d=128, cp=1)
+    args = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), 0] + [ALIGNED] * 11 + [0]
+    assert L.cpattn_backward(*args) == C.CPATTN_ESHAPE
+    sargs = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), C.CPATTN_CAUSAL] + \
+        [ALIGNED] * 10 + [0]
+    assert L.cpattn_step_bwd(*sargs) == C.CPATTN_ESHAPE
+    d2 = _dims(b=1, s=1 << 30, hq=8192, hkv=8, d=128, cp=1)
+    assert L.cpattn_bwd_delta(ctypes.byref(d2), ALIGNED, ALIGNED, ALIGNED, 0) == C.CPATTN_ESHAPE
 
 
 def test_forward_steps_validation():

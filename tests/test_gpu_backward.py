@@ -63,10 +63,14 @@ WIDE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp40
                               hq=4, hkv=2, cp=40)
 ONE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp1", s=400, hq=4,
                              hkv=2, cp=1)
-EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP}
+# more ranks than one merge pass takes (64), chunks of 3 rows
+FINE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp128",
+                              s=2 * 128 * 3, hq=4, hkv=2, cp=128)
+EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP, "cp128": FINE_CP}
 
 
-@pytest.mark.parametrize("name,s", REDUCED + [("cp40", WIDE_CP.s), ("cp1", ONE_CP.s)])
+@pytest.mark.parametrize("name,s", REDUCED + [("cp40", WIDE_CP.s), ("cp1", ONE_CP.s),
+                                              ("cp128", FINE_CP.s)])
 def test_backward_all_ranks_reduced(name, s):
     w = EXTRA[name] if name in EXTRA else small(WORKLOADS[name], s)
     say(f"backward reduced {name} s={s}")

@@ -62,26 +62,5 @@ def run_rank(P: CPProblem, rank, out_dtype=C.CPATTN_F32):
     return host_f32(buf["o"]), buf["lse"].cpu().numpy()
 
 
-def oracle_sampled_rows(w: Workload, q, k, v, positions):
-    """Oracle output of the global rows ``positions`` (all heads)."""
-    positions = np.asarray(positions)
-    qf = as_f32(q[:, positions]).astype(np.float64)
-    hi = int(positions.max()) + 1
-    kf = as_f32(k[:, :hi]).astype(np.float64)
-    vf = as_f32(v[:, :hi]).astype(np.float64)
-    if w.rope_theta is not None:
-        qf = ocp.rope(qf, positions, w.rope_theta)
-        kf = ocp.rope(kf, np.arange(hi), w.rope_theta)
-    return attention_rows(qf, kf, vf, positions + 1)
-
-
-def sample_local_rows(c, n_mid, seed):
-    """Local row indices: both chunk edges plus n_mid random rows."""
-    rng = np.random.default_rng(seed)
-    edges = [0, 1, c - 1, c, c + 1, 2 * c - 1]
-    mid = rng.choice(2 * c, size=n_mid, replace=False)
-    return np.unique(np.concatenate([edges, mid]))
-
-
 __all__ = ["C", "CPProblem", "Workload", "make_inputs", "to_device", "torch", "np", "ocp",
            "attention_rows", "causal_attention", "as_f32"]

@@ -4,8 +4,7 @@ vs the non-CP oracle and vs the step-wise entry point.
 
 * every bf16 workload at a reduced length (ragged chunks and tiles, GQA,
   MHA, RoPE, b = 2): every rank, every row, every head vs the oracle;
-* every bf16 workload at its full size: sampled rows (chunk edges plus
-  random rows) of every rank (the RoPE workload: its measured rank);
+* every bf16 workload at its full size, every row: test_gpu_full_size.py;
 * the fused and the step-wise results agree within the bf16 bound on the
   whole share; the bf16 output is the fp32 output within one rounding;
   lse_out = NULL leaves O unchanged; cp = 1 is plain causal attention.
@@ -14,8 +13,7 @@ import numpy as np
 import pytest
 
 from gpu_helpers import (BF16_MAX_ABS, BF16_MEAN_ABS, C, CPProblem, assert_close, host_f32,
-                         make_inputs, ocp, oracle_full, oracle_sampled_rows, run_rank,
-                         sample_local_rows, say, small, torch)
+                         make_inputs, ocp, oracle_full, run_rank, say, small, torch)
 from long_context_causal_amd.inputs import WORKLOADS
 
 pytestmark = pytest.mark.gpu
@@ -82,26 +80,3 @@ def test_fused_matches_stepwise_and_options():
     assert np.all(np.abs(ob - o32) <= np.abs(o32) * 2.0 ** -8 + 1e-30), "bf16 output rounding"
     on, _ = run_fused(P, r, with_lse=False)
     assert np.array_equal(on, o32), "lse_out = NULL changed O"
-
-
-FULL = [("bf16_gqa_s8k_cp4", 12), ("bf16_mha_s16k_cp4_widelogits", 8),
-        ("bf16_gqa_s32k_cp8", 6), ("bf16_gqa_s128k_cp16_rope", 24)]
-
-
-@pytest.mark.parametrize("name,n_mid", FULL)
-def test_fused_full_size_sampled_rows(name, n_mid):
-    w = WORKLOADS[name]
-    say(f"fused full {name}: inputs")
-    q, k, v = make_inputs(w)
-    P = CPProblem(w, q, k, v)
-    P.partition()
-    ranks = [w.rank] if w.rope_theta is not None else list(range(w.cp))
-    for r in ranks:
-        say(f"  rank {r}: gpu")
-        o, l = run_fused(P, r)
-        rows = sample_local_rows(w.c, n_mid, seed=200 + r)
-        pos = ocp.zigzag_positions(w.s, w.cp, r)[rows]
-        say(f"  rank {r}: oracle on {len(rows)} rows")
-        o_ref, l_ref = oracle_sampled_rows(w, q, k, v, pos)
-        assert_close(f"rank {r} O", o[:, rows], o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
-        assert_close(f"rank {r} L", l[:, :, rows], l_ref, 1e-3)

@@ -8,6 +8,7 @@ Every ``csrc/*.hip`` and ``csrc/*.cpp`` is compiled to an object under
 import concurrent.futures
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -37,16 +38,43 @@ COMMON = [
 ]
 
 
+# Per-kernel resource remarks: the build refuses any kernel that spills to
+# scratch.  The attention kernels complete their direct global -> LDS copies
+# with hand-counted vmcnt waits, which are only right while the compiler
+# issues no vector-memory instruction of its own inside their loops; a spill
+# would add such instructions silently.
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def scratch_users(remarks: str) -> list:
+    """(kernel, bytes per lane) of every kernel whose remarks report a
+    nonzero ScratchSize."""
+    found, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None and int(m.group(1)) > 0:
+            found.append((name, int(m.group(1))))
+    return found
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    device = src.endswith(".hip")
+    cmd = [hipcc(), *COMMON, *([RESOURCE_REMARKS] if device else []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "remark:")
+    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise))
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    spills = scratch_users(res.stderr)
+    if spills:
+        raise RuntimeError(f"{src}: kernels use scratch memory (register spills): {spills}")
     if err.strip() and verbose:
         print(err, flush=True)
     return obj

@@ -82,13 +82,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // One direct global -> LDS copy of 16 bytes per lane from base + off (base
 // wave-uniform, in SGPRs; off a per-lane byte offset); lane L writes
-// lds_base + 16*L.  m0 carries the LDS base; one wait state separates its
-// write from the copy that reads it.
+// lds_base + 16*L.  m0 carries the LDS base (declared clobbered, so the
+// compiler keeps nothing of its own there across the copy); one wait state
+// separates its write from the copy that reads it.
 __device__ __forceinline__ void dma16(const void *base, unsigned off, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(off), "s"(base), "s"(lds_base)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // One direct global -> LDS copy of 4 bytes per lane from the lane's own
@@ -97,7 +98,7 @@ __device__ __forceinline__ void dma4(const void *addr, unsigned lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(addr), "s"(lds_base)
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Waits for the wave's LDS operations, then for every wave of the workgroup.

@@ -50,6 +50,10 @@ def parse():
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the per-rank and per-configuration step timings")
+    ap.add_argument("--digest", metavar="DIR", default=None,
+                    help="write the profiles/ summaries from rocprofv3 csv output under DIR "
+                         "(DIR/trace: kernel trace; DIR/p1, DIR/p2: FETCH_SIZE, WRITE_SIZE; "
+                         "DIR/p3: SQ counters; see PROFILE_COMMANDS) and exit")
     return ap.parse_args()
 
 
@@ -77,15 +81,10 @@ def committed_traffic(workload, key="attention_traffic_bytes_per_launch"):
     with (KERNEL_SOURCES, concatenated); if they have changed since, the
     figure no longer describes this kernel and None is returned.
     """
-    import hashlib
     prof = os.path.join(ROOT, "profiles", f"attn_steps_bf16__{workload}__hbm_traffic.txt")
     if not os.path.exists(prof):
         return None
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "long_context_causal_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    digest = h.hexdigest()
+    digest = _kernel_source_digest()
     recorded, traffic = None, None
     with open(prof) as f:
         for line in f:
@@ -158,6 +157,39 @@ def share_step_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
     return flops / (steps * 1e-3) / 1e12, flops / (whole * 1e-3) / 1e12
 
 
+def split_gbps(torch, P, w, stream, reps=5):
+    """The split of Q, K and V (RoPE on Q and K where the workload has it)
+    in GB/s of algorithmic bytes: in a warm loop, and each launch after a
+    512 MB scratch write that evicts the 256 MB last-level cache (medians)."""
+    import numpy as np
+    es = 2 if w.dtype == "bf16" else 4
+    nbytes = 2 * w.b * w.s * (w.hq + 2 * w.hkv) * w.d * es + 4 * w.s
+    q_bytes = 2 * w.b * w.s * w.hq * w.d * es
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    hot, cold, q_only = [], [], []
+    with torch.cuda.stream(stream):
+        P.partition(stream)
+        for rep in range(2 * reps):
+            if rep >= reps:
+                scratch.fill_(1)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            P.partition_one("q", stream)
+            e[1].record(stream)
+            P.partition_one("k", stream)
+            P.partition_one("v", stream)
+            e[2].record(stream)
+            (cold if rep >= reps else hot).append((e[0], e[2]))
+            q_only.append((e[0], e[1]))
+        torch.cuda.synchronize()
+    del scratch
+    med = lambda ev: float(np.median([a.elapsed_time(b) for a, b in ev]))
+    return {"rope": w.rope_theta is not None, "bytes": nbytes,
+            "gbps": round(nbytes / (med(hot) * 1e-3) / 1e9, 1),
+            "cold_cache_gbps": round(nbytes / (med(cold) * 1e-3) / 1e9, 1),
+            "q_gbps": round(q_bytes / (med(q_only) * 1e-3) / 1e9, 1)}
+
+
 def peak_check(C, torch, stream, iters=10000, rounds=4):
     """The bf16 MFMA rate this part sustains on a pure matrix stream (random
     operands, two waves per SIMD, one workgroup per CU at a time, 'rounds'
@@ -192,8 +224,207 @@ def peak_check(C, torch, stream, iters=10000, rounds=4):
                      "(cpattn_probe_mfma)"}
 
 
+# --- rocprofv3 summaries (python bench.py --digest DIR) ------------------------
+
+# the commands whose csv output --digest reads (run from the repository root)
+_BENCH = "python3 bench.py --steps {steps} --warmup {warmup} --cpu-sample-seconds 0"
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {dir}/trace -o run -- "
+             + _BENCH.format(steps=10, warmup=3),
+    "p1": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {dir}/p1 -o run -- "
+          + _BENCH.format(steps=2, warmup=1),
+    "p2": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {dir}/p2 -o run -- "
+          + _BENCH.format(steps=2, warmup=1),
+    "p3": "rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS "
+          "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE "
+          "--output-format csv -d {dir}/p3 -o run -- " + _BENCH.format(steps=2, warmup=1),
+}
+# a partition_copy workgroup (256 lanes) moves 4096 16-byte vectors: its
+# dispatch reads and writes exactly 256 bytes per lane of its grid (every
+# workload here splits into whole workgroups)
+COPY_BYTES_PER_LANE = 256
+
+
+def _short_kernel(name):
+    name = name.replace("cpattn::(anonymous namespace)::", "")
+    return name[5:].split("(")[0] if name.startswith("void ") else name.split("(")[0]
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def steps_grid_lanes(w, rank):
+    """Grid size (lanes) of the rank's steps grid: 256-row query tiles of
+    every step x hq x b workgroups of 512 lanes."""
+    c = w.c
+    tiles = 0
+    for i in range(w.cp):
+        rows = c if i > rank else 2 * c          # q_second_half steps hold c rows
+        tiles += (rows + 255) // 256
+    return tiles * w.hq * w.b * 512
+
+
+def fused_grid_lanes(w):
+    return (2 * w.c + 255) // 256 * w.hq * w.b * 512
+
+
+def _kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_causal_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def digest(prof_dir):
+    """The three profiles/ summaries of the headline workload from the csv
+    output of PROFILE_COMMANDS under prof_dir."""
+    import collections
+    import statistics
+    from long_context_causal_amd.inputs import HEADLINE, WORKLOADS
+    w = WORKLOADS[HEADLINE]
+    src = _kernel_source_digest()
+    cmd = {k: v.format(dir=prof_dir) for k, v in PROFILE_COMMANDS.items()}
+    mean = statistics.mean
+    out_files = {}
+
+    # kernel trace: durations per kernel and per (kernel, grid)
+    trace = _csv_rows(os.path.join(prof_dir, "trace"), "kernel_trace.csv")
+    byg = collections.defaultdict(list)
+    for r in trace:
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        byg[(_short_kernel(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(dur)
+    lines = [f"# rocprofv3 kernel trace (durations in us), {w.name} and the other bf16 workloads",
+             f"# command (repository root, MI355X): {cmd['trace']}",
+             f"# summary: python3 bench.py --digest {prof_dir}",
+             f"# kernel source sha256 ({' + '.join(KERNEL_SOURCES)}): {src}", "",
+             f"{'kernel':34s} {'grid_lanes':>11s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} "
+             f"{'max_us':>10s}"]
+    for (k, g), v in sorted(byg.items()):
+        lines.append(f"{k:34s} {g:11d} {len(v):6d} {mean(v) / 1e3:10.2f} {min(v) / 1e3:10.2f} "
+                     f"{max(v) / 1e3:10.2f}")
+    lines.append("")
+    for name in (HEADLINE, "bf16_gqa_s8k_cp4", "bf16_mha_s16k_cp4_widelogits",
+                 "bf16_gqa_s128k_cp16_rope"):
+        wc = WORKLOADS[name]
+        g = steps_grid_lanes(wc, wc.rank)
+        v = byg.get(("attn_steps_bf16", g))
+        if v:
+            lines.append(f"{name} rank {wc.rank}: attn_steps_bf16 grid {g}: {len(v)} launches, "
+                         f"mean {mean(v) / 1e3:.2f} us, {wc.rank_flops():.4e} FLOP per launch, "
+                         f"{wc.rank_flops() / mean(v) * 1e-3:.1f} TFLOP/s")
+    v = byg.get(("attn_steps_bf16", steps_grid_lanes(w, w.rank)))
+    if v:
+        lines.append(f"attention_avg_launch_us: {mean(v) / 1e3:.3f}")
+        lines.append(f"attention_tflops_from_trace: {w.rank_flops() / mean(v) * 1e-3:.1f}")
+    fv = [d for (k, g), ds in byg.items() if k.startswith("attn_fused_bf16")
+          and g == fused_grid_lanes(w) for d in ds]
+    if fv:
+        lines.append(f"fused_avg_launch_us: {mean(fv) / 1e3:.3f}")
+        lines.append(f"fused_tflops_from_trace: {w.rank_flops() / mean(fv) * 1e-3:.1f}")
+    out_files[f"attn_steps_bf16__{w.name}__kernel_trace.txt"] = lines
+
+    # HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), scaled by
+    # what they read for the plain copies of known size
+    def counters(sub):
+        d = collections.defaultdict(list)
+        for r in _csv_rows(os.path.join(prof_dir, sub), "counter_collection.csv"):
+            d[(_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]), r["Counter_Name"])].append(
+                float(r["Counter_Value"]))
+        return d
+    fetch, write = counters("p1"), counters("p2")
+    cal = []
+    for (k, g, c), v in sorted(fetch.items()):
+        if k == "partition_copy" and c == "FETCH_SIZE":
+            true_kib = g * COPY_BYTES_PER_LANE / 1024
+            wv = write.get((k, g, "WRITE_SIZE"))
+            if wv:
+                cal.append((g, true_kib, mean(v), mean(wv)))
+    f_fetch = mean(t / f for _, t, f, _ in cal)
+    f_write = mean(t / wr for _, t, _, wr in cal)
+    lines = [f"# HBM traffic counters per dispatch (KiB), {w.name}",
+             f"# command 1: {cmd['p1']}", f"# command 2: {cmd['p2']}",
+             f"# summary: python3 bench.py --digest {prof_dir}",
+             f"# kernel source sha256 ({' + '.join(KERNEL_SOURCES)}): {src}",
+             "# calibration: every partition_copy dispatch is a plain copy that reads and "
+             f"writes {COPY_BYTES_PER_LANE} bytes per lane of its grid",
+             f"# {'grid_lanes':>10s} {'true_KiB':>10s} {'FETCH_KiB':>10s} {'WRITE_KiB':>10s} "
+             f"{'true/FETCH':>10s} {'true/WRITE':>10s}"]
+    for g, t, f, wr in cal:
+        lines.append(f"# {g:10d} {t:10.0f} {f:10.0f} {wr:10.0f} {t / f:10.4f} {t / wr:10.4f}")
+    lines += [f"fetch_scale: {f_fetch:.4f}", f"write_scale: {f_write:.4f}",
+              f"fetch_scale_spread: {min(t / f for _, t, f, _ in cal):.4f}"
+              f"..{max(t / f for _, t, f, _ in cal):.4f}",
+              f"write_scale_spread: {min(t / wr for _, t, _, wr in cal):.4f}"
+              f"..{max(t / wr for _, t, _, wr in cal):.4f}", "",
+              f"{'kernel':34s} {'grid_lanes':>11s} {'n':>3s} {'FETCH_KiB':>12s} "
+              f"{'WRITE_KiB':>12s} {'scaled_MB':>10s}"]
+    scaled_of = {}
+    for (k, g, c), v in sorted(fetch.items()):
+        if c != "FETCH_SIZE":
+            continue
+        wv = write.get((k, g, "WRITE_SIZE"))
+        if not wv:
+            continue
+        scaled = (mean(v) * f_fetch + mean(wv) * f_write) * 1024
+        scaled_of[(k, g)] = scaled
+        lines.append(f"{k:34s} {g:11d} {len(v):3d} {mean(v):12.0f} {mean(wv):12.0f} "
+                     f"{scaled / 1e6:10.1f}")
+    lines.append("")
+    a = scaled_of.get(("attn_steps_bf16", steps_grid_lanes(w, w.rank)))
+    if a is not None:
+        lines.append(f"attention_traffic_bytes_per_launch: {a:.0f}")
+    fz = [b for (k, g), b in scaled_of.items() if k.startswith("attn_fused_bf16")
+          and g == fused_grid_lanes(w)]
+    if fz:
+        lines.append(f"fused_traffic_bytes_per_launch: {mean(fz):.0f}")
+    out_files[f"attn_steps_bf16__{w.name}__hbm_traffic.txt"] = lines
+
+    # SQ counters: instruction mix and MFMA busy fraction per (kernel, grid)
+    sq = counters("p3")
+    lines = [f"# SQ counters per dispatch (sums over the device), bf16 workloads",
+             f"# command: {cmd['p3']}", f"# summary: python3 bench.py --digest {prof_dir}",
+             f"# kernel source sha256 ({' + '.join(KERNEL_SOURCES)}): {src}"]
+    names = sorted({c for (_, _, c) in sq})
+    for k, g in sorted({(k, g) for (k, g, _) in sq}):
+        lines.append(f"{k} grid={g}")
+        for c in names:
+            v = sq.get((k, g, c))
+            if v:
+                lines.append(f"   {c:28s} {mean(v):16.0f}")
+        mf, busy, gui = (sq.get((k, g, c)) for c in
+                         ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"))
+        if mf and busy and gui and mean(mf) > 0:
+            # GRBM_GUI_ACTIVE sums the 8 XCDs; MFMA busy sums the 1024 SIMDs
+            lines.append(f"   mfma_busy_fraction (busy per SIMD / active cycles per XCD): "
+                         f"{mean(busy) / 1024 / (mean(gui) / 8):.3f}")
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS"):
+                if sq.get((k, g, c)):
+                    lines.append(f"   {c.lower()[9:]}_per_mfma: {mean(sq[(k, g, c)]) / mean(mf):.2f}")
+    out_files[f"attn_steps_bf16__{w.name}__sq_counters.txt"] = lines
+
+    for fname, text in out_files.items():
+        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
+            f.write("\n".join(text) + "\n")
+        print(f"wrote profiles/{fname}")
+
+
 def main():
     args = parse()
+    if args.digest:
+        digest(args.digest)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(collectives are out of scope); run with --gpus 1", file=sys.stderr)
@@ -492,7 +723,8 @@ def main():
             a_tf, w_tf = share_step_tflops(C, torch, Pc, wc, wc.rank, stream)
             configs[name] = {"rank": wc.rank, "attention_tflops": round(a_tf, 2),
                              "frac": round(a_tf / peak, 4),
-                             "steps_plus_merge_tflops": round(w_tf, 2)}
+                             "steps_plus_merge_tflops": round(w_tf, 2),
+                             "partition": split_gbps(torch, Pc, wc, stream)}
             del Pc
             torch.cuda.empty_cache()
         line["configs"] = configs

@@ -19,10 +19,11 @@
 //
 // Without RoPE the kernel is a pure HBM copy: each workgroup moves a run of
 // whole output rows with 16-byte loads and stores, consecutive lanes on
-// consecutive addresses.  With RoPE each workgroup first builds the row's
-// cos/sin table in LDS (angles pos * theta^(-2t/d) in fp64, sincos in fp64,
-// rounded to fp32), then rotates the pairs (t, t + d/2) of every head in
-// fp32 and rounds the result to the element type (bf16: nearest even).
+// consecutive addresses.  With RoPE each workgroup takes a run of rows too:
+// it builds the run's cos/sin table in LDS (angles pos * theta^(-2t/d) in
+// fp64, sincos in fp64, rounded to fp32), then rotates the pairs (t, t +
+// d/2) of every head in fp32, 16-byte vectors at a time, and rounds the
+// result to the element type (bf16: nearest even).
 #include "internal.h"
 
 #include <math.h>
@@ -134,6 +135,7 @@ struct RopeParams {
     int32_t *pos;
     int64_t s, tloc, b, rows_total;
     int cp, h, d;
+    int rows_per_block;
     double theta;
     SeqTable tab;
 };
@@ -156,33 +158,90 @@ __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
-// One output row per loop iteration of the workgroup.
+constexpr int MAX_ROPE_ROWS = 64;      // rows per workgroup
+constexpr int MAX_HALF = 64;           // d / 2
+
+// A run of whole output rows per workgroup, as the copy kernel.  The
+// workgroup first finds each row's source row and position, then fills a
+// table of the run's cos and sin (angles in fp64, rounded to fp32; the
+// inverse frequencies theta^(-2t/d) once per workgroup), then rotates: a
+// lane takes the 16-byte vector at dims [e, e + EV) of one head together
+// with its partner at [e + d/2, e + d/2 + EV) (the rotate-half pairs),
+// both read with 16-byte loads, four pairs in flight, and writes both
+// rotated vectors with 16-byte stores.
 template <typename T>
 __global__ void __launch_bounds__(NT) partition_rope(RopeParams<T> p) {
-    extern __shared__ float cs[];   // [d/2] cos, then [d/2] sin
+    constexpr int EV = 16 / sizeof(T);          // elements per 16-byte vector
+    __shared__ int64_t srow[MAX_ROPE_ROWS];     // source element offset of each row
+    __shared__ double inv_freq[MAX_HALF];
+    __shared__ float cs[MAX_ROPE_ROWS][MAX_HALF];
+    __shared__ float sn[MAX_ROPE_ROWS][MAX_HALF];
+    __shared__ int32_t rpos[MAX_ROPE_ROWS];
     const int half = p.d / 2;
-    for (int64_t row = blockIdx.x; row < p.rows_total; row += gridDim.x) {
+    const int64_t row0 = (int64_t)blockIdx.x * p.rows_per_block;
+    const int nrows = (int)min((int64_t)p.rows_per_block, p.rows_total - row0);
+    for (int rr = threadIdx.x; rr < nrows; rr += NT) {
         int64_t r, n, j, sp, gp;
-        split_row(row, p.b, p.tloc, r, n, j);
+        split_row(row0 + rr, p.b, p.tloc, r, n, j);
         source_row(p.tab, p.cp, r, j, sp, gp);
-        __syncthreads();
-        for (int t = threadIdx.x; t < half; t += NT) {
-            const double inv_freq = pow(p.theta, -2.0 * (double)t / (double)p.d);
-            double sn, cn;
-            sincos((double)gp * inv_freq, &sn, &cn);
-            cs[t] = (float)cn;
-            cs[half + t] = (float)sn;
+        srow[rr] = (n * p.s + sp) * (int64_t)p.h * p.d;
+        rpos[rr] = (int32_t)gp;
+    }
+    for (int t = threadIdx.x; t < half; t += NT)
+        inv_freq[t] = pow(p.theta, -2.0 * (double)t / (double)p.d);
+    __syncthreads();
+    for (int e = threadIdx.x; e < nrows * half; e += NT) {
+        const int rr = e / half, t = e - rr * half;
+        double sv, cv;
+        sincos((double)rpos[rr] * inv_freq[t], &sv, &cv);
+        cs[rr][t] = (float)cv;
+        sn[rr][t] = (float)sv;
+    }
+    __syncthreads();
+
+    // tasks: (row of the run, head, vector pair) with the pair fastest
+    const int pairs = half / EV;
+    const int per_row = p.h * pairs;
+    const int ntask = nrows * per_row;
+    const __attribute__((address_space(1))) u32x4 *xg =
+        (const __attribute__((address_space(1))) u32x4 *)p.x;
+    __attribute__((address_space(1))) u32x4 *zg = (__attribute__((address_space(1))) u32x4 *)p.xz;
+    constexpr int U = 4;
+    for (int i0 = 0; i0 < ntask; i0 += U * NT) {
+        u32x4 lo[U], hi[U];
+        int64_t dst[U];
+        int rrow[U], tt[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            // lanes past the last task repeat it (their stores are skipped)
+            const int task = min(i0 + k * NT + (int)threadIdx.x, ntask - 1);
+            const int rr = task / per_row;
+            const int rem = task - rr * per_row;
+            const int hh = rem / pairs, jp = rem - hh * pairs;
+            const int64_t off = (int64_t)hh * p.d + jp * EV;   // element offset in the row
+            lo[k] = xg[(srow[rr] + off) / EV];
+            hi[k] = xg[(srow[rr] + off + half) / EV];
+            dst[k] = ((row0 + rr) * (int64_t)p.h * p.d + off) / EV;
+            rrow[k] = rr;
+            tt[k] = jp * EV;
         }
-        __syncthreads();
-        const T *src = p.x + (n * p.s + sp) * (int64_t)p.h * p.d;
-        T *dst = p.xz + row * (int64_t)p.h * p.d;
-        for (int i = threadIdx.x; i < p.h * half; i += NT) {
-            const int hh = i / half, t = i - hh * half;
-            const float x1 = to_f32(src[hh * p.d + t]);
-            const float x2 = to_f32(src[hh * p.d + half + t]);
-            const float cn = cs[t], sn = cs[half + t];
-            dst[hh * p.d + t] = from_f32<T>(x1 * cn - x2 * sn);
-            dst[hh * p.d + half + t] = from_f32<T>(x2 * cn + x1 * sn);
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (i0 + k * NT + (int)threadIdx.x >= ntask) continue;
+            const T *a = (const T *)&lo[k];
+            const T *bq = (const T *)&hi[k];
+            u32x4 olo, ohi;
+            T *ya = (T *)&olo;
+            T *yb = (T *)&ohi;
+#pragma unroll
+            for (int e = 0; e < EV; ++e) {
+                const float x1 = to_f32(a[e]), x2 = to_f32(bq[e]);
+                const float cn = cs[rrow[k]][tt[k] + e], s1 = sn[rrow[k]][tt[k] + e];
+                ya[e] = from_f32<T>(x1 * cn - x2 * s1);
+                yb[e] = from_f32<T>(x2 * cn + x1 * s1);
+            }
+            zg[dst[k]] = olo;
+            zg[dst[k] + half / EV] = ohi;
         }
     }
     if (p.pos != nullptr && blockIdx.x == 0) write_positions(p.tab, p.cp, p.tloc, p.pos);
@@ -216,17 +275,21 @@ hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const Seq
         hipLaunchKernelGGL(partition_copy, dim3((unsigned)blocks), dim3(NT), 0, stream, p);
         return hipGetLastError();
     }
-    const int64_t blocks = rows_total < 65536 ? rows_total : 65536;
-    const size_t shmem = sizeof(float) * dims.d;
+    // runs of whole rows, about 64 KiB of input per workgroup
+    const int64_t row_bytes = (int64_t)h * dims.d * es;
+    int rpb = (int)(65536 / row_bytes);
+    rpb = rpb < 1 ? 1 : (rpb > MAX_ROPE_ROWS ? MAX_ROPE_ROWS : rpb);
+    if (dims.d / 2 > MAX_HALF || (dims.d / 2) % (16 / es) != 0) return hipErrorInvalidValue;
+    const int64_t blocks = (rows_total + rpb - 1) / rpb;
     if (dtype == CPATTN_BF16) {
         RopeParams<uint16_t> p{(const uint16_t *)x, (uint16_t *)xz, pos, dims.s, tloc, dims.b,
-                               rows_total, dims.cp, h, dims.d, rope->theta, tab};
-        hipLaunchKernelGGL(partition_rope<uint16_t>, dim3((unsigned)blocks), dim3(NT), shmem,
+                               rows_total, dims.cp, h, dims.d, rpb, rope->theta, tab};
+        hipLaunchKernelGGL(partition_rope<uint16_t>, dim3((unsigned)blocks), dim3(NT), 0,
                            stream, p);
     } else {
         RopeParams<float> p{(const float *)x, (float *)xz, pos, dims.s, tloc, dims.b,
-                            rows_total, dims.cp, h, dims.d, rope->theta, tab};
-        hipLaunchKernelGGL(partition_rope<float>, dim3((unsigned)blocks), dim3(NT), shmem,
+                            rows_total, dims.cp, h, dims.d, rpb, rope->theta, tab};
+        hipLaunchKernelGGL(partition_rope<float>, dim3((unsigned)blocks), dim3(NT), 0,
                            stream, p);
     }
     return hipGetLastError();

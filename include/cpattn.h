@@ -224,6 +224,23 @@ int cpattn_forward(const cpattn_dims *dims, int dtype, float scale, int rank,
                    size_t ws_bytes, int out_dtype, void *o_out, float *lse_out,
                    void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc): cpattn_forward
+ * without a workspace argument.  The step partials live in a scratch array
+ * inside the library, CPATTN_NOALLOC_SCRATCH_BYTES per device, which every
+ * GPU the library runs on holds from the library's load until the process
+ * ends.  The call allocates nothing; the caller still passes the inputs and
+ * outputs, and the stream must belong to the current device.  ENOSPACE if
+ * the share's workspace (cpattn_forward_workspace) exceeds the array;
+ * otherwise arguments, results and errors as cpattn_forward, bit for bit.
+ * Every call on a device shares that device's array and leaves the last
+ * call's partials in it: calls that overlap on one device (two streams, or
+ * two host threads) race, and the caller must serialise them. */
+#define CPATTN_NOALLOC_SCRATCH_BYTES (256u << 20)
+int cpattn_forward_noalloc(const cpattn_dims *dims, int dtype, float scale, int rank,
+                           const void *qz, const void *kz, const void *vz, int out_dtype,
+                           void *o_out, float *lse_out, void *stream);
+
 /* One rank's whole forward share in one launch, device ("超大规模集群…":
  * the rank's big and small attention run concurrently; "Megatron-LM 篇" 3.2
  * step 2 and its per-step LSE correction).  Each query row's online softmax

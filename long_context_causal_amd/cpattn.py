@@ -23,6 +23,7 @@ CPATTN_Q_SECOND_HALF = 2
 CPATTN_OK, CPATTN_EINVAL, CPATTN_ESHAPE, CPATTN_EDTYPE, CPATTN_EALIGN, \
     CPATTN_ENOSPACE, CPATTN_EHIP = range(7)
 CPATTN_MERGE_PASS = 64
+CPATTN_NOALLOC_SCRATCH_BYTES = 256 << 20
 CPATTN_MAX_SEQS = 128
 
 
@@ -88,6 +89,7 @@ def lib():
         L.cpattn_forward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, ctypes.c_size_t,
                                      I, P, P, P]
         L.cpattn_forward_fused.argtypes = [D, I, ctypes.c_float, I, P, P, P, I, P, P, P]
+        L.cpattn_forward_noalloc.argtypes = [D, I, ctypes.c_float, I, P, P, P, I, P, P, P]
         V = ctypes.POINTER(cpattn_varlen)
         L.cpattn_partition_positions_varlen.argtypes = [ctypes.c_int64, I, I, V,
                                                         ctypes.POINTER(ctypes.c_int32)]
@@ -106,7 +108,7 @@ def lib():
         for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
                      "cpattn_step_fwd", "cpattn_merge", "cpattn_forward_partials",
                      "cpattn_forward_steps", "cpattn_forward",
-                     "cpattn_forward_fused", "cpattn_bwd_delta", "cpattn_step_bwd",
+                     "cpattn_forward_fused", "cpattn_forward_noalloc", "cpattn_bwd_delta", "cpattn_step_bwd",
                      "cpattn_backward", "cpattn_partition_positions_varlen",
                      "cpattn_partition_varlen", "cpattn_forward_fused_varlen",
                      "cpattn_backward_varlen", "cpattn_probe_mfma", "cpattn_device_info"):
@@ -209,6 +211,14 @@ def cpattn_forward(dims, dtype, scale, rank, qz, kz, vz, ws, ws_bytes, out_dtype
                                 _ptr(kz), _ptr(vz), _ptr(ws), int(ws_bytes), out_dtype,
                                 _ptr(o_out), _ptr(lse_out), _stream(stream)),
            "cpattn_forward")
+
+
+def cpattn_forward_noalloc(dims, dtype, scale, rank, qz, kz, vz, out_dtype, o_out, lse_out=None,
+                           stream=None):
+    _check(lib().cpattn_forward_noalloc(ctypes.byref(dims), dtype, float(scale), rank, _ptr(qz),
+                                        _ptr(kz), _ptr(vz), out_dtype, _ptr(o_out),
+                                        _ptr(lse_out), _stream(stream)),
+           "cpattn_forward_noalloc")
 
 
 def cpattn_forward_fused(dims, dtype, scale, rank, qz, kz, vz, out_dtype, o_out, lse_out=None,

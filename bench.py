@@ -124,10 +124,45 @@ def cpu_baseline(w, q, k, v, rank, target_s):
     dt = run(sample)
     flops = float((4 * w.d * w.hq * w.b * (sample + 1)).sum())
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": host_cpu_model(),
+            "host_logical_cpus": os.cpu_count(),
             "sample": f"rank {rank}: every {stride}th of its {len(pos_all)} local rows "
                       f"({len(sample)} rows x {w.hq} heads x b={w.b}, all visible keys), "
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64"}
+
+
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def share_fused_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
+    """TFLOP/s of the fused launch (cpattn_forward_fused) of one rank's
+    share, from HIP events on ``stream`` (median)."""
+    import numpy as np
+    out = P.alloc_out(rank, C.CPATTN_F32)
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            P.forward_fused(out, stream)
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            P.forward_fused(out, stream)
+            e[1].record(stream)
+            ev.append(e)
+        torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del out
+    return w.rank_flops() / (ms * 1e-3) / 1e12
 
 
 def share_step_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
@@ -724,6 +759,8 @@ def main():
             configs[name] = {"rank": wc.rank, "attention_tflops": round(a_tf, 2),
                              "frac": round(a_tf / peak, 4),
                              "steps_plus_merge_tflops": round(w_tf, 2),
+                             "fused_tflops": round(share_fused_tflops(C, torch, Pc, wc, wc.rank,
+                                                                      stream), 2),
                              "partition": split_gbps(torch, Pc, wc, stream)}
             del Pc
             torch.cuda.empty_cache()

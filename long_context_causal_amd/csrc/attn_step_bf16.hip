@@ -138,6 +138,13 @@ struct StepPlan {
     __device__ __forceinline__ TileRef tile(int u) const {
         return TileRef{kb, vb, min(u, ntiles - 1) * BN, nk, CAUSAL, 0};
     }
+    // tile u from tile u - 1 (the same as tile(u), without its arithmetic)
+    __device__ __forceinline__ TileRef next(const TileRef &a, int u) const {
+        if (u >= ntiles) return a;
+        TileRef t = a;
+        t.key0 += BN;
+        return t;
+    }
     // whether the wave whose rows start at wrow0 computes tile t: causal
     // waves stop after their diagonal
     __device__ __forceinline__ bool comp(int t, int wrow0) const {
@@ -154,11 +161,21 @@ struct StepPlan {
 // segments are streamed only when some row of the workgroup is one of
 // those); rank r, keys [0, min(2c, q0 + BM)) causal (step 0).  A segment
 // whose length is not a multiple of BN ends in a masked tile.
+// floor(u / d) for 0 <= u, 1 <= d < 2^31, with m = floor((2^32 - 1) / d): the
+// high product is floor(u / d) or one less, and one compare settles it (so the
+// per-tile segment lookups cost a few scalar instructions, not a division).
+__device__ __forceinline__ int div_by(int u, unsigned m, int d) {
+    int q = (int)__umulhi((unsigned)u, m);
+    if (u - q * d >= d) ++q;
+    return q;
+}
+
 struct FusedPlan {
     static constexpr bool kLongestFirst = true;     // later tiles: second chunk, causal
     const uint16_t *k0, *v0;      // rank 0's block, this batch and KV head
     int64_t block;                // elements between consecutive ranks' blocks
     int r, cp, c, cA, nAB, cB, ta, tb, kend, ntiles, q0;
+    unsigned mA, mB;              // div_by multipliers of cA and cB
     int qtile, qrow0, nq, orow0, orows;
     __device__ __forceinline__ void init(const Params &p, int qt, int n, int g) {
         const int i = seq_of(p.tab.tile0, p.tab.nseq, qt);
@@ -177,6 +194,8 @@ struct FusedPlan {
         q0 = qtile * BM;
         cA = (c + BN - 1) / BN;
         cB = (2 * c + BN - 1) / BN;
+        mA = 0xFFFFFFFFu / (unsigned)cA;
+        mB = 0xFFFFFFFFu / (unsigned)cB;
         nAB = (q0 + BM > c) ? cp - 1 - r : 0;
         ta = r * cA;
         tb = ta + nAB * cB;
@@ -186,17 +205,39 @@ struct FusedPlan {
     __device__ __forceinline__ TileRef tile(int u) const {
         u = min(u, ntiles - 1);
         if (u < ta) {
-            const int seg = u / cA;
+            const int seg = div_by(u, mA, cA);
             const int64_t off = (int64_t)(r - 1 - seg) * block;
             return TileRef{k0 + off, v0 + off, (u - seg * cA) * BN, c, false, 0};
         }
         if (u < tb) {
-            const int seg = (u - ta) / cB;
+            const int seg = div_by(u - ta, mB, cB);
             const int64_t off = (int64_t)(cp - 1 - seg) * block;
             return TileRef{k0 + off, v0 + off, (u - ta - seg * cB) * BN, 2 * c, false, c};
         }
         const int64_t off = (int64_t)r * block;
         return TileRef{k0 + off, v0 + off, (u - tb) * BN, kend, true, 0};
+    }
+    // tile u from tile u - 1 (the same as tile(u), without the segment
+    // lookup): the next tile of the segment, or the first of the next one
+    __device__ __forceinline__ TileRef next(const TileRef &a, int u) const {
+        if (u >= ntiles) return a;
+        if (u == tb) {
+            const int64_t off = (int64_t)r * block;
+            return TileRef{k0 + off, v0 + off, 0, kend, true, 0};
+        }
+        if (u == ta) {
+            const int64_t off = (int64_t)(cp - 1) * block;
+            return TileRef{k0 + off, v0 + off, 0, 2 * c, false, c};
+        }
+        TileRef t = a;
+        if (a.key0 + BN < a.nk) {
+            t.key0 += BN;
+        } else {   // next block of the same kind: one rank lower
+            t.kb -= block;
+            t.vb -= block;
+            t.key0 = 0;
+        }
+        return t;
     }
     __device__ __forceinline__ bool comp(int t, int wrow0) const {
         if (t < 0 || wrow0 >= nq) return false;   // a wave past the sample's rows idles
@@ -399,13 +440,14 @@ struct Kernel {
     // consumes its own reads, and the reads a wave issues ahead of the
     // barrier touch stages that no copy in flight or issued here overwrites.
     __device__ __forceinline__ static void sync(const Plan &P, State &S, int h,
-                                                unsigned lds_addr, int wave) {
+                                                unsigned lds_addr, int wave, TileRef &cpy) {
         const bool even = (h & 1) == 0;
         wait_vmcnt<LPT>();
         asm volatile("s_barrier" ::: "memory");
         if (even) {
             const int u = (h >> 1) + 2;
-            issue(S, lds_addr + (u % NS) * 2 * TILEB, P.tile(u), wave);
+            cpy = P.next(cpy, u);
+            issue(S, lds_addr + (u % NS) * 2 * TILEB, cpy, wave);
         }
     }
 
@@ -489,8 +531,11 @@ struct Kernel {
         // prologue: tiles 0 and 1 in flight, then Q; one full wait before the
         // loop (tile 0 has to land first anyway) also tells the compiler that
         // Q is resident, so it puts no memory wait inside the loop
-        issue(S, lds_addr, P.tile(0), wave);
-        issue(S, lds_addr + 2 * TILEB, P.tile(1), wave);
+        // tile cursors: cpy is the last tile copied (tiles 0 and 1 here, then
+        // tile u + 2 after barrier 2u), cur the tile of the softmax phase
+        TileRef cpy = P.tile(1), cur = P.tile(0);
+        issue(S, lds_addr, cur, wave);
+        issue(S, lds_addr + 2 * TILEB, cpy, wave);
         {
             const int row = min(wrow0 + l32, P.nq - 1);
             const uint16_t *src =
@@ -515,18 +560,19 @@ struct Kernel {
         // zero, so a following G adds nothing for it.
         // The zero stage's writes complete before the first barrier.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        sync(P, S, 0, lds_addr, wave);
+        sync(P, S, 0, lds_addr, wave, cpy);
         Ahead A;
         read_ahead(S, A);
-        if (grp == 1) sync(P, S, 1, lds_addr, wave);
+        if (grp == 1) sync(P, S, 1, lds_addr, wave, cpy);
         for (int t = 0; t <= ntiles; ++t) {
             const int hg = 2 * t + grp;    // the barrier this wave last passed
             if (P.comp(t, wrow0) || P.comp(t - 1, wrow0))
                 matrix_phase(S, A);
             if (t == ntiles) break;
-            sync(P, S, hg + 1, lds_addr, wave);
+            sync(P, S, hg + 1, lds_addr, wave, cpy);
+            if (t > 0) cur = P.next(cur, t);
             if (P.comp(t, wrow0)) {
-                softmax_phase(p, S, P.tile(t), wrow0, lane);
+                softmax_phase(p, S, cur, wrow0, lane);
             } else {
 #pragma unroll
                 for (int kc = 0; kc < BN / 16; ++kc)
@@ -546,9 +592,9 @@ struct Kernel {
             }
             // K(t+1) is resident since barrier 2t+1, V(t) since barrier 2t
             read_ahead(S, A);
-            sync(P, S, hg + 2, lds_addr, wave);
+            sync(P, S, hg + 2, lds_addr, wave, cpy);
         }
-        if (grp == 0) sync(P, S, 2 * ntiles + 1, lds_addr, wave);
+        if (grp == 0) sync(P, S, 2 * ntiles + 1, lds_addr, wave, cpy);
         // copies issued past the end land in stages nobody reads; retire them
         // before the workgroup's LDS is handed to the next workgroup
         wait_vmcnt<0>();
@@ -601,29 +647,39 @@ struct StepDesc {
     const uint16_t *k, *v;   // the source rank's block
     float *o, *lse;          // the step's partial
     int q_row0, nq, nk, causal, num_qtiles;
-    int item0;               // first workgroup of the step within one (batch, KV head)
+};
+// Query tiles of one step that stream the same number of key tiles (every
+// tile of a non-causal step; one tile, or a run of neighbouring tiles, of the
+// causal step), in workgroup order: tile qt0, qt0 + dir, ...
+struct WorkRun {
+    int step, qt0, dir;
+    int item0;               // first workgroup of the run within one (batch, KV head)
 };
 constexpr int MAX_STEPS = 32;   // steps per launch (kernel argument space)
+constexpr int MAX_RUNS = 64;
 struct StepsParams {
     const uint16_t *q;
     int64_t two_c;
-    int hq, hkv, group, nsteps, items;   // items: workgroups per (batch, KV head)
+    int hq, hkv, group, nruns, items;   // items: workgroups per (batch, KV head)
     float scale_log2;
     StepDesc st[MAX_STEPS];
+    WorkRun run[MAX_RUNS];
 };
+static_assert(sizeof(StepsParams) <= 4096, "kernel arguments");
 
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_steps_bf16(StepsParams sp) {
     __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
-    // workgroup -> (batch, KV head), then the step, then (query tile, head
-    // in group) inside the step; the steps are laid out longest items first
+    // workgroup -> (batch, KV head), then the run, then (query tile, head in
+    // group) inside it; the runs are laid out longest first across all steps
     const int item = xcd_order(blockIdx.x, gridDim.x);
     const int ng = item / sp.items;
     int w = item - ng * sp.items;
     int j = 0;
-    while (j + 1 < sp.nsteps && sp.st[j + 1].item0 <= w) ++j;
-    const StepDesc &d = sp.st[j];
-    w -= d.item0;
+    while (j + 1 < sp.nruns && sp.run[j + 1].item0 <= w) ++j;
+    const WorkRun &r = sp.run[j];
+    w -= r.item0;
+    const StepDesc &d = sp.st[r.step];
     Params p = {};
     p.q = sp.q;
     p.k = d.k;
@@ -639,12 +695,12 @@ attn_steps_bf16(StepsParams sp) {
     p.group = sp.group;
     p.num_qtiles = d.num_qtiles;
     p.scale_log2 = sp.scale_log2;
-    const int hh = w % sp.group, qt_rank = w / sp.group;
+    const int hh = w % sp.group, qt = r.qt0 + r.dir * (w / sp.group);
     const int g = ng % sp.hkv, n = ng / sp.hkv;
     if (d.causal)
-        Kernel<StepPlan<true>, false>::run_item(p, lds, n, g, hh, d.num_qtiles - 1 - qt_rank);
+        Kernel<StepPlan<true>, false>::run_item(p, lds, n, g, hh, qt);
     else
-        Kernel<StepPlan<false>, false>::run_item(p, lds, n, g, hh, qt_rank);
+        Kernel<StepPlan<false>, false>::run_item(p, lds, n, g, hh, qt);
 }
 
 // A rank's whole share (merged output, fp32 or bf16).
@@ -690,16 +746,6 @@ hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void
                              hipStream_t stream) {
     static_assert(MAX_STEPS == STEPS_PER_GRID, "one grid takes the steps of one call");
     if (n < 1 || n > MAX_STEPS) return hipErrorInvalidValue;
-    // longest workgroups first: the steps whose query tiles stream the most
-    // key tiles (q_second_half: 2c keys; kv_first_half: c keys), then the
-    // causal step, whose own tiles run from its longest to its shortest
-    int order[MAX_STEPS];
-    int m = 0;
-    for (int pass = 0; pass < 3; ++pass)
-        for (int i = 0; i < n; ++i) {
-            const int cls = g[i].causal ? 2 : (g[i].nk >= g[i].nq ? 0 : 1);
-            if (cls == pass) order[m++] = i;
-        }
     StepsParams sp = {};
     sp.q = (const uint16_t *)q;
     sp.two_c = g[0].two_c;
@@ -707,11 +753,14 @@ hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void
     sp.hkv = g[0].hkv;
     sp.group = g[0].hq / g[0].hkv;
     sp.scale_log2 = g[0].scale_log2;
-    sp.nsteps = n;
-    int items = 0;
-    for (int jj = 0; jj < n; ++jj) {
-        const int i = order[jj];
-        StepDesc &d = sp.st[jj];
+    // runs of query tiles with their key-tile counts: a non-causal step is
+    // one run; the causal step's tiles (query tile qt sees keys up to
+    // 256(qt+1)) are one run each, or runs of neighbours when there are
+    // more tiles than the run table holds
+    int len[MAX_RUNS], cnt[MAX_RUNS], nr = 0, ncausal = 0;
+    for (int i = 0; i < n; ++i) ncausal += g[i].causal ? 1 : 0;
+    for (int i = 0; i < n; ++i) {
+        StepDesc &d = sp.st[i];
         d.k = (const uint16_t *)k[i];
         d.v = (const uint16_t *)v[i];
         d.o = o[i];
@@ -721,9 +770,38 @@ hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void
         d.nk = (int)g[i].nk;
         d.causal = g[i].causal ? 1 : 0;
         d.num_qtiles = (int)((g[i].nq + BM - 1) / BM);
-        d.item0 = items;
-        items += d.num_qtiles * sp.group;
+        if (!d.causal) {
+            sp.run[nr] = WorkRun{i, 0, 1, 0};
+            len[nr] = (d.nk + BN - 1) / BN;
+            cnt[nr++] = d.num_qtiles;
+            continue;
+        }
+        const int room = (MAX_RUNS - (n - ncausal)) / ncausal;   // runs this step may take
+        const int per = (d.num_qtiles + room - 1) / room;        // tiles per run
+        for (int qt = d.num_qtiles - 1; qt >= 0; qt -= per) {
+            sp.run[nr] = WorkRun{i, qt, -1, 0};
+            len[nr] = (min(d.nk, (qt + 1) * BM) + BN - 1) / BN;
+            cnt[nr++] = min(per, qt + 1);
+        }
     }
+    // longest first (stable: ties keep step order)
+    for (int a = 1; a < nr; ++a)
+        for (int b2 = a; b2 > 0 && len[b2 - 1] < len[b2]; --b2) {
+            const WorkRun tr = sp.run[b2];
+            sp.run[b2] = sp.run[b2 - 1];
+            sp.run[b2 - 1] = tr;
+            const int tl = len[b2], tc = cnt[b2];
+            len[b2] = len[b2 - 1];
+            cnt[b2] = cnt[b2 - 1];
+            len[b2 - 1] = tl;
+            cnt[b2 - 1] = tc;
+        }
+    int items = 0;
+    for (int a = 0; a < nr; ++a) {
+        sp.run[a].item0 = items;
+        items += cnt[a] * sp.group;
+    }
+    sp.nruns = nr;
     sp.items = items;
     const int64_t blocks = (int64_t)items * sp.hkv * g[0].b;
     hipLaunchKernelGGL(attn_steps_bf16, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, sp);

@@ -334,12 +334,36 @@ def digest(prof_dir):
     mean = statistics.mean
     out_files = {}
 
+    # the fused launches of the headline share and of the 128k share have the
+    # same grid; the headline's come before the first backward dispatch, the
+    # 128k share's after the first dispatch of its steps grid (bench order)
+    def windows(rows, grid_key):
+        first = lambda pred: min((int(r["Dispatch_Id"]) for r in rows if pred(r)),
+                                 default=1 << 62)
+        bwd = first(lambda r: _short_kernel(r["Kernel_Name"]).startswith("attn_bwd"))
+        w5 = WORKLOADS["bf16_gqa_s128k_cp16_rope"]
+        g5 = steps_grid_lanes(w5, w5.rank)
+        c5 = first(lambda r: _short_kernel(r["Kernel_Name"]) == "attn_steps_bf16"
+                   and int(r[grid_key]) == g5)
+        return bwd, c5
+
+    def fused_of(rows, grid_key, w_name, value):
+        """Values of the fused dispatches of one workload's share."""
+        bwd, c5 = windows(rows, grid_key)
+        g = fused_grid_lanes(WORKLOADS[w_name])
+        lo, hi = (c5, 1 << 62) if w_name == "bf16_gqa_s128k_cp16_rope" else (0, bwd)
+        if w_name not in (HEADLINE, "bf16_gqa_s128k_cp16_rope"):
+            lo, hi = 0, 1 << 62
+        return [value(r) for r in rows
+                if _short_kernel(r["Kernel_Name"]).startswith("attn_fused_bf16")
+                and int(r[grid_key]) == g and lo <= int(r["Dispatch_Id"]) < hi]
+
     # kernel trace: durations per kernel and per (kernel, grid)
     trace = _csv_rows(os.path.join(prof_dir, "trace"), "kernel_trace.csv")
     byg = collections.defaultdict(list)
+    dur_of = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     for r in trace:
-        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        byg[(_short_kernel(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(dur)
+        byg[(_short_kernel(r["Kernel_Name"]), int(r["Grid_Size_X"]))].append(dur_of(r))
     lines = [f"# rocprofv3 kernel trace (durations in us), {w.name} and the other bf16 workloads",
              f"# command (repository root, MI355X): {cmd['trace']}",
              f"# summary: python3 bench.py --digest {prof_dir}",
@@ -349,6 +373,7 @@ def digest(prof_dir):
     for (k, g), v in sorted(byg.items()):
         lines.append(f"{k:34s} {g:11d} {len(v):6d} {mean(v) / 1e3:10.2f} {min(v) / 1e3:10.2f} "
                      f"{max(v) / 1e3:10.2f}")
+    lines.append("(grids shared by two workloads are split by dispatch order below)")
     lines.append("")
     for name in (HEADLINE, "bf16_gqa_s8k_cp4", "bf16_mha_s16k_cp4_widelogits",
                  "bf16_gqa_s128k_cp16_rope"):
@@ -359,12 +384,16 @@ def digest(prof_dir):
             lines.append(f"{name} rank {wc.rank}: attn_steps_bf16 grid {g}: {len(v)} launches, "
                          f"mean {mean(v) / 1e3:.2f} us, {wc.rank_flops():.4e} FLOP per launch, "
                          f"{wc.rank_flops() / mean(v) * 1e-3:.1f} TFLOP/s")
+        fv = fused_of(trace, "Grid_Size_X", name, dur_of)
+        if fv:
+            lines.append(f"{name} rank {wc.rank}: attn_fused_bf16 grid {fused_grid_lanes(wc)}: "
+                         f"{len(fv)} launches, mean {mean(fv) / 1e3:.2f} us, "
+                         f"{wc.rank_flops() / mean(fv) * 1e-3:.1f} TFLOP/s")
     v = byg.get(("attn_steps_bf16", steps_grid_lanes(w, w.rank)))
     if v:
         lines.append(f"attention_avg_launch_us: {mean(v) / 1e3:.3f}")
         lines.append(f"attention_tflops_from_trace: {w.rank_flops() / mean(v) * 1e-3:.1f}")
-    fv = [d for (k, g), ds in byg.items() if k.startswith("attn_fused_bf16")
-          and g == fused_grid_lanes(w) for d in ds]
+    fv = fused_of(trace, "Grid_Size_X", HEADLINE, dur_of)
     if fv:
         lines.append(f"fused_avg_launch_us: {mean(fv) / 1e3:.3f}")
         lines.append(f"fused_tflops_from_trace: {w.rank_flops() / mean(fv) * 1e-3:.1f}")
@@ -374,11 +403,12 @@ def digest(prof_dir):
     # what they read for the plain copies of known size
     def counters(sub):
         d = collections.defaultdict(list)
-        for r in _csv_rows(os.path.join(prof_dir, sub), "counter_collection.csv"):
+        rows = _csv_rows(os.path.join(prof_dir, sub), "counter_collection.csv")
+        for r in rows:
             d[(_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]), r["Counter_Name"])].append(
                 float(r["Counter_Value"]))
-        return d
-    fetch, write = counters("p1"), counters("p2")
+        return d, rows
+    (fetch, fetch_rows), (write, write_rows) = counters("p1"), counters("p2")
     cal = []
     for (k, g, c), v in sorted(fetch.items()):
         if k == "partition_copy" and c == "FETCH_SIZE":
@@ -420,14 +450,17 @@ def digest(prof_dir):
     a = scaled_of.get(("attn_steps_bf16", steps_grid_lanes(w, w.rank)))
     if a is not None:
         lines.append(f"attention_traffic_bytes_per_launch: {a:.0f}")
-    fz = [b for (k, g), b in scaled_of.items() if k.startswith("attn_fused_bf16")
-          and g == fused_grid_lanes(w)]
-    if fz:
-        lines.append(f"fused_traffic_bytes_per_launch: {mean(fz):.0f}")
+    ff = fused_of([r for r in fetch_rows if r["Counter_Name"] == "FETCH_SIZE"], "Grid_Size",
+                  HEADLINE, lambda r: float(r["Counter_Value"]))
+    fw = fused_of([r for r in write_rows if r["Counter_Name"] == "WRITE_SIZE"], "Grid_Size",
+                  HEADLINE, lambda r: float(r["Counter_Value"]))
+    if ff and fw:
+        lines.append(f"fused_traffic_bytes_per_launch: "
+                     f"{(mean(ff) * f_fetch + mean(fw) * f_write) * 1024:.0f}")
     out_files[f"attn_steps_bf16__{w.name}__hbm_traffic.txt"] = lines
 
     # SQ counters: instruction mix and MFMA busy fraction per (kernel, grid)
-    sq = counters("p3")
+    sq, _ = counters("p3")
     lines = [f"# SQ counters per dispatch (sums over the device), bf16 workloads",
              f"# command: {cmd['p3']}", f"# summary: python3 bench.py --digest {prof_dir}",
              f"# kernel source sha256 ({' + '.join(KERNEL_SOURCES)}): {src}"]

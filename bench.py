@@ -131,6 +131,23 @@ def cpu_baseline(w, q, k, v, rank, target_s):
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64"}
 
 
+# The engine clock ramps up over a fraction of a second of load after the
+# GPU has idled (e.g. while the host draws the next workload's inputs); a
+# leg that timed its kernels right after an idle spell measured them up to
+# 25% slow.  Every timed leg first runs its own work for PREWARM_S seconds,
+# untimed, then its warm-up steps.
+PREWARM_S = 1.0
+
+
+def prewarm(torch, fn, seconds=PREWARM_S):
+    """Runs fn (which enqueues GPU work) repeatedly for about ``seconds``."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def host_cpu_model():
     """The host CPU's model name (from /proc/cpuinfo), or None."""
     try:
@@ -149,6 +166,7 @@ def share_fused_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
     import numpy as np
     out = P.alloc_out(rank, C.CPATTN_F32)
     with torch.cuda.stream(stream):
+        prewarm(torch, lambda: P.forward_fused(out, stream))
         for _ in range(warmup):
             P.forward_fused(out, stream)
         torch.cuda.synchronize()
@@ -171,6 +189,7 @@ def share_step_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):
     import numpy as np
     buf = P.alloc_rank(rank, C.CPATTN_F32)
     with torch.cuda.stream(stream):
+        prewarm(torch, lambda: (P.steps(buf, stream), P.merge(buf, stream)))
         for _ in range(warmup):
             P.steps(buf, stream)
             P.merge(buf, stream)
@@ -203,7 +222,7 @@ def split_gbps(torch, P, w, stream, reps=5):
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     hot, cold, q_only = [], [], []
     with torch.cuda.stream(stream):
-        P.partition(stream)
+        prewarm(torch, lambda: P.partition(stream), 0.5)
         for rep in range(2 * reps):
             if rep >= reps:
                 scratch.fill_(1)
@@ -527,6 +546,7 @@ def main():
         mark("merge")
 
     with torch.cuda.stream(stream):
+        prewarm(torch, one_step)
         for _ in range(args.warmup):
             one_step()
         torch.cuda.synchronize()
@@ -560,6 +580,7 @@ def main():
     # the same steps launched one by one (cpattn_step_fwd), each timed
     per_step = None
     with torch.cuda.stream(stream):
+        prewarm(torch, lambda: [P.step(buf, i, stream) for i in range(w.cp)])
         for _ in range(args.warmup):
             for i in range(w.cp):
                 P.step(buf, i, stream)
@@ -581,6 +602,7 @@ def main():
     if w.dtype == "bf16":
         fout = P.alloc_out(rank, C.CPATTN_F32)
         with torch.cuda.stream(stream):
+            prewarm(torch, lambda: (P.partition(stream), P.forward_fused(fout, stream)))
             for _ in range(args.warmup):
                 P.partition(stream)
                 P.forward_fused(fout, stream)
@@ -607,6 +629,7 @@ def main():
         Pv = CPProblem(w, P.q, P.k, P.v, cu_seqlens=cu)
         vout = Pv.alloc_out(rank, C.CPATTN_F32)
         with torch.cuda.stream(stream):
+            prewarm(torch, lambda: (Pv.partition(stream), Pv.forward_fused(vout, stream)))
             for _ in range(args.warmup):
                 Pv.partition(stream)
                 Pv.forward_fused(vout, stream)
@@ -632,6 +655,7 @@ def main():
         do_v = torch.randn(vout["o"].shape, generator=gen_v, device="cuda").to(torch.bfloat16)
         gv = Pv.alloc_grads(rank)
         with torch.cuda.stream(stream):
+            prewarm(torch, lambda: Pv.backward(gv, vout["o"], vout["lse"], do_v, stream))
             for _ in range(args.warmup):
                 Pv.backward(gv, vout["o"], vout["lse"], do_v, stream)
             torch.cuda.synchronize()
@@ -658,6 +682,7 @@ def main():
         do_r = torch.randn(buf["o"].shape, generator=gen, device="cuda").to(torch.bfloat16)
         grads = P.alloc_grads(rank)
         with torch.cuda.stream(stream):
+            prewarm(torch, lambda: P.backward(grads, buf["o"], buf["lse"], do_r, stream))
             for _ in range(args.warmup):
                 P.backward(grads, buf["o"], buf["lse"], do_r, stream)
             torch.cuda.synchronize()

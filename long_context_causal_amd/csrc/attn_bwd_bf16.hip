@@ -190,24 +190,25 @@ constexpr int NSQ = 4;
 constexpr int PDQ = NSQ - 1;
 constexpr int STAGE_DQ = 2 * TB;           // K, V
 
-// A run of 32-key tiles a dQ workgroup streams for its query rows: the K, V
-// base of the block (this batch element and KV head, at the sample's first
-// key), the tile's first key, the keys of the block visible in the segment,
-// whether the causal mask applies (key <= row, both from the sample start),
-// and the first row of the sample that sees the segment.
-struct DqTile {
+// A cursor over the 32-key tiles a dQ workgroup streams for its query rows,
+// one step per tile: the K, V base of the current key block (this batch
+// element and KV head, at the sample's first key), the tile's first key, the
+// block's keys streamed (rows past them repeat its last), and which rows see
+// the block: every row, only rows >= c (the second chunk), or rows >= key
+// (causal, both counted from the sample start).
+enum : int { SEE_ALL = 0, SEE_SECOND = 1, SEE_CAUSAL = 2 };
+struct DqCursor {
     const uint16_t *kb, *vb;
-    int key0, nk;
-    bool causal;
-    int min_row;
+    int key0, nk, see, left;   // left: blocks of this kind after the current one
 };
 
 // One step (cpattn_step_bwd's dq launch): the sample's rows and keys of the
-// step's mode, one segment.
+// step's mode, one block.
 struct DqStepPlan {
     const uint16_t *kb, *vb;
     int qrow0, nq, nk, ntiles;
     bool causal;
+    static constexpr int c = 0;   // no block is seen by the second chunk only
     __device__ __forceinline__ void init(const BwdParams &p, int smp, int q0, int n, int g) {
         const Geo G = geo_of(p, smp, p.mode);
         qrow0 = G.qrow0;
@@ -219,18 +220,15 @@ struct DqStepPlan {
         const int kend = causal ? min(nk, q0 + TR * NWB) : nk;
         ntiles = (kend + TR - 1) / TR;
     }
-    __device__ __forceinline__ DqTile tile(int t) const {
-        return DqTile{kb, vb, min(t, ntiles - 1) * TR, nk, causal, 0};
+    __device__ __forceinline__ DqCursor first() const {
+        return DqCursor{kb, vb, 0, nk, causal ? SEE_CAUSAL : SEE_ALL, 0};
     }
-    __device__ __forceinline__ bool comp(int t, int wrow0) const {
-        if (wrow0 >= nq) return false;   // a wave past the last row idles
-        return causal ? t < min(ntiles, (wrow0 + TR - 1) / TR + 1) : t < ntiles;
-    }
+    __device__ __forceinline__ void next(DqCursor &C) const { C.key0 += TR; }
 };
 
 // A rank's whole share for one query tile (the dq of all cp steps in one
 // grid): the sample's 2c local rows, and in streaming order the key
-// segments of its steps -- steps 1 .. r (kv_first_half: keys [0, c) of the
+// blocks of its steps -- steps 1 .. r (kv_first_half: keys [0, c) of the
 // blocks of ranks r-1 .. 0), steps r+1 .. cp-1 (q_second_half: keys
 // [0, 2c) of ranks cp-1 .. r+1, seen by rows c .. 2c-1 only; streamed only
 // when the tile has such rows), then step 0 (the rank's own block,
@@ -238,9 +236,8 @@ struct DqStepPlan {
 struct DqSharePlan {
     const uint16_t *k0, *v0;
     int64_t block;
-    int r, cp, c, cA, cB, nAB, ta, tb, kend, ntiles;
+    int r, cp, c, nAB, kend, ntiles;
     int qrow0, nq;
-    bool causal;   // unused: masks come per tile
     __device__ __forceinline__ void init(const BwdParams &p, int smp, int q0, int n, int g) {
         const int l0 = p.tab.lcu[smp];
         c = (p.tab.lcu[smp + 1] - l0) >> 1;
@@ -251,35 +248,38 @@ struct DqSharePlan {
         block = p.block_elems;
         r = p.rank;
         cp = p.cp;
-        cA = (c + TR - 1) / TR;
-        cB = (2 * c + TR - 1) / TR;
+        const int cA = (c + TR - 1) / TR, cB = (2 * c + TR - 1) / TR;
         nAB = (q0 + TR * NWB > c) ? cp - 1 - r : 0;
-        ta = r * cA;
-        tb = ta + nAB * cB;
         kend = min(2 * c, q0 + TR * NWB);
-        ntiles = tb + (kend + TR - 1) / TR;
-        causal = false;
+        ntiles = r * cA + nAB * cB + (kend + TR - 1) / TR;
     }
-    __device__ __forceinline__ DqTile tile(int u) const {
-        u = min(u, ntiles - 1);
-        if (u < ta) {
-            const int seg = u / cA;
-            const int64_t off = (int64_t)(r - 1 - seg) * block;
-            return DqTile{k0 + off, v0 + off, (u - seg * cA) * TR, c, false, 0};
-        }
-        if (u < tb) {
-            const int seg = (u - ta) / cB;
-            const int64_t off = (int64_t)(cp - 1 - seg) * block;
-            return DqTile{k0 + off, v0 + off, (u - ta - seg * cB) * TR, 2 * c, false, c};
+    __device__ __forceinline__ DqCursor block_of(int see) const {
+        if (see == SEE_SECOND) {
+            const int64_t off = (int64_t)(cp - 1) * block;
+            return DqCursor{k0 + off, v0 + off, 0, 2 * c, SEE_SECOND, nAB - 1};
         }
         const int64_t off = (int64_t)r * block;
-        return DqTile{k0 + off, v0 + off, (u - tb) * TR, kend, true, 0};
+        return DqCursor{k0 + off, v0 + off, 0, kend, SEE_CAUSAL, 0};
     }
-    __device__ __forceinline__ bool comp(int t, int wrow0) const {
-        if (wrow0 >= nq) return false;   // a wave past the sample's rows idles
-        if (t < ta) return true;
-        if (t < tb) return wrow0 + TR - 1 >= c;
-        return t - tb < min(ntiles - tb, (wrow0 + TR - 1) / TR + 1);
+    __device__ __forceinline__ DqCursor first() const {
+        if (r > 0) {
+            const int64_t off = (int64_t)(r - 1) * block;
+            return DqCursor{k0 + off, v0 + off, 0, c, SEE_ALL, r - 1};
+        }
+        return block_of(nAB > 0 ? SEE_SECOND : SEE_CAUSAL);
+    }
+    // the next tile (only called while one is left)
+    __device__ __forceinline__ void next(DqCursor &C) const {
+        C.key0 += TR;
+        if (C.key0 < C.nk) return;
+        if (C.left > 0) {   // the block of the next lower rank, same kind
+            --C.left;
+            C.kb -= block;
+            C.vb -= block;
+            C.key0 = 0;
+            return;
+        }
+        C = block_of(C.see == SEE_ALL && nAB > 0 ? SEE_SECOND : SEE_CAUSAL);
     }
 };
 
@@ -338,37 +338,73 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
 
     const int64_t row_bytes = (int64_t)p.hkv * D * 2;
     const unsigned coff = copy_offset(lane, wave, row_bytes);   // m = wave, wave + 4
-    // tiles past the last repeat it, so every wave issues 4 copies per tile
-    auto issue = [&](int t, int stage) {
-        const DqTile T = P.tile(t);
+    // copy cursor (tile cu); tiles past the last repeat it, so every wave
+    // issues 4 copies per tile
+    DqCursor CC = P.first();
+    int cu = 0;
+    auto issue = [&](int stage) {
         const unsigned sb = lbase + stage * STAGE_DQ;
+        if (CC.key0 + TR <= CC.nk) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            copy_rows(T.kb, row_bytes, T.key0, T.nk, wave + 4 * i, coff, sb, lane);
-            copy_rows(T.vb, row_bytes, T.key0, T.nk, wave + 4 * i, coff, sb + TB, lane);
+            for (int i = 0; i < 2; ++i) {
+                const int m = wave + 4 * i;
+                dma16((const char *)CC.kb + (CC.key0 + 4 * m) * row_bytes, coff, sb + m * 1024);
+                dma16((const char *)CC.vb + (CC.key0 + 4 * m) * row_bytes, coff,
+                      sb + TB + m * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                copy_rows(CC.kb, row_bytes, CC.key0, CC.nk, wave + 4 * i, coff, sb, lane);
+                copy_rows(CC.vb, row_bytes, CC.key0, CC.nk, wave + 4 * i, coff, sb + TB, lane);
+            }
+        }
+    };
+    auto advance = [&]() {
+        if (cu + 1 < ntiles) {
+            ++cu;
+            P.next(CC);
         }
     };
     if (ntiles > 0) {
 #pragma unroll
-        for (int i = 0; i < PDQ; ++i) issue(i, i);
+        for (int i = 0; i < PDQ; ++i) {
+            issue(i);
+            advance();
+        }
         wait_vmcnt<4 * (PDQ - 1)>();
     }
     lds_barrier();
+    // the lane's LDS read offsets in a tile (the stage base is added per read)
+    unsigned ro[D / 16], to[D / 32][2];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) ro[kk] = L.roff(kk);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        to[dt][0] = L.toff(dt, 0);
+        to[dt][1] = L.toff(dt, 1);
+    }
+    DqCursor T = P.first();   // compute cursor: tile t
     int stage = 0;
+    const bool rows_live = wrow0 < P.nq;   // a wave past the sample's rows idles
+    const int c_half = P.c;
     for (int t = 0; t < ntiles; ++t) {
         int ns = stage + PDQ;
         if (ns >= NSQ) ns -= NSQ;
-        issue(t + PDQ, ns);
-        if (P.comp(t, wrow0)) {
-            const DqTile T = P.tile(t);
+        issue(ns);
+        advance();
+        const bool comp = rows_live && (T.see == SEE_ALL ||
+                                        (T.see == SEE_SECOND ? wrow0 + TR - 1 >= c_half
+                                                             : T.key0 <= wrow0));
+        if (comp) {
             const unsigned sK = lbase + stage * STAGE_DQ, sV = sK + TB;
             // the tile's LDS operands are read ahead of the products
             // (the transposed K^T reads go out behind the S, dP products)
             bf16x8 ak[D / 16], av[D / 16], at[2][D / 32];
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                ak[kk] = k_read(sK + L.roff(kk));
-                av[kk] = k_read(sV + L.roff(kk));
+                ak[kk] = k_read(sK + ro[kk]);
+                av[kk] = k_read(sV + ro[kk]);
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x16 s = {}, dp = {};
@@ -382,13 +418,14 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
             for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-                    at[kc][dt] = vt_read2(sK + L.toff(dt, 0) + kc * 16 * RB,
-                                          sK + L.toff(dt, 1) + kc * 16 * RB);
+                    at[kc][dt] = vt_read2(sK + to[dt][0] + kc * 16 * RB,
+                                          sK + to[dt][1] + kc * 16 * RB);
             __builtin_amdgcn_sched_barrier(0);
             const int key0 = T.key0;
             // tile entirely visible to the wave's rows: no mask
-            const bool full = key0 + TR <= T.nk && (!T.causal || key0 + TR - 1 <= wrow0) &&
-                              wrow0 >= T.min_row;
+            const bool full = key0 + TR <= T.nk &&
+                              (T.see != SEE_CAUSAL || key0 + TR - 1 <= wrow0) &&
+                              (T.see != SEE_SECOND || wrow0 >= c_half);
             bf16x8 dsb[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
@@ -399,8 +436,8 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int key = key0 + 16 * kc + 8 * hi + e;
-                        const bool vis = key < T.nk && (!T.causal || key <= qrow) &&
-                                         qrow >= T.min_row;
+                        const bool vis = key < T.nk && (T.see != SEE_CAUSAL || key <= qrow) &&
+                                         (T.see != SEE_SECOND || qrow >= c_half);
                         x[e] = vis ? x[e] : -INFINITY;
                     }
                 }
@@ -420,6 +457,7 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
         wait_vmcnt<4 * (PDQ - 1)>();   // tile t + 1 has landed
         lds_barrier();
         stage = stage + 1 == NSQ ? 0 : stage + 1;
+        if (t + 1 < ntiles) P.next(T);
     }
     wait_vmcnt<0>();
 
@@ -535,43 +573,86 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
     const int per_head = max(nqt - qstart, 0);
     const int ntiles = per_head * hpw;
     const int64_t row_bytes = (int64_t)p.hq * D * 2;
+    const int64_t row_step = TR * row_bytes;
+    const int row_first = qstart * TR, row_end = nqt * TR;
     const unsigned coff = copy_offset(lane, wave, row_bytes);
-    const int64_t qrow_base = (int64_t)n * p.two_c + G.qrow0;   // row of the sample's query 0
-    // lanes 0-31 copy L, lanes 32-63 D; the per-lane base is settled here so
-    // no wait for its load is left inside the tile loop
-    const float *ld_base = hi ? p.delta : p.lse;
-    settle(ld_base);
-    // tiles past the last repeat it, so every wave issues 3 copies per tile
-    auto issue = [&](int u, int stage) {
-        u = min(u, ntiles - 1);
-        const int head = h0 + u / per_head;
-        const int row0 = (qstart + u % per_head) * TR;
+    // Copy cursor: tile cu of the workgroup (heads in turn, rows in 32-row
+    // tiles), as byte pointers to its first row in Q and dO and the index
+    // of that row's L and D.  Tiles past the last repeat it, so every wave
+    // issues 3 copies per tile.
+    int cu = 0, cr0 = row_first;
+    const int64_t hrow0 = (int64_t)n * p.two_c + G.qrow0;   // row of the sample's query 0
+    const char *cq = (const char *)(p.q + (hrow0 * p.hq + h0) * D) + row_first * row_bytes;
+    const char *cdo = (const char *)(p.dout + (hrow0 * p.hq + h0) * D) + row_first * row_bytes;
+    int64_t cli = ((int64_t)n * p.hq + h0) * p.two_c + G.qrow0 + row_first;
+    // lanes 0-31 copy L, lanes 32-63 D (the same layout); the per-lane base
+    // is settled here so no wait for its load is left inside the tile loop
+    const float *ld_lane = (hi ? p.delta : p.lse) + l32;
+    settle(ld_lane);
+    auto issue = [&](int stage) {
         const unsigned sb = lbase + stage * STAGE_DKDV;
-        const int64_t e0 = qrow_base * p.hq * D + (int64_t)head * D;
-        copy_rows(p.q + e0, row_bytes, row0, G.nq, wave, coff, sb, lane);
-        copy_rows(p.dout + e0, row_bytes, row0, G.nq, wave, coff, sb + TB, lane);
-        const int lr = min(row0 + l32, G.nq - 1);
-        const int64_t li = ((int64_t)n * p.hq + head) * p.two_c + G.qrow0 + lr;
-        dma4(ld_base + li, sb + 2 * TB + wave * LD_SLOT);
+        const unsigned sld = sb + 2 * TB + wave * LD_SLOT;
+        if (cr0 + TR <= G.nq) {
+            dma16(cq + 4 * wave * row_bytes, coff, sb + wave * 1024);
+            dma16(cdo + 4 * wave * row_bytes, coff, sb + TB + wave * 1024);
+            dma4(ld_lane + cli, sld);
+        } else {
+            // the last tile of a head crosses the sample's last row: rows
+            // past it repeat it
+            const int64_t back = (int64_t)cr0 * row_bytes;
+            copy_rows((const uint16_t *)(cq - back), row_bytes, cr0, G.nq, wave, coff, sb, lane);
+            copy_rows((const uint16_t *)(cdo - back), row_bytes, cr0, G.nq, wave, coff, sb + TB,
+                      lane);
+            dma4(ld_lane - l32 + (cli - cr0) + min(cr0 + l32, G.nq - 1), sld);
+        }
+    };
+    auto advance = [&]() {
+        if (cu + 1 >= ntiles) return;
+        ++cu;
+        cr0 += TR;
+        cq += row_step;
+        cdo += row_step;
+        cli += TR;
+        if (cr0 >= row_end) {   // next head
+            const int64_t rows = row_end - row_first;
+            cr0 = row_first;
+            cq += 2 * D - rows * row_bytes;
+            cdo += 2 * D - rows * row_bytes;
+            cli += p.two_c - rows;
+        }
     };
     if (ntiles > 0) {
 #pragma unroll
-        for (int i = 0; i < PDK; ++i) issue(i, i);
+        for (int i = 0; i < PDK; ++i) {
+            issue(i);
+            advance();
+        }
         wait_vmcnt<3 * (PDK - 1)>();
     }
     lds_barrier();
+    // The lane's LDS read offsets in a tile (the stage base is added per read).
+    unsigned ro[D / 16], to[D / 32][2];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) ro[kk] = L.roff(kk);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        to[dt][0] = L.toff(dt, 0);
+        to[dt][1] = L.toff(dt, 1);
+    }
     // Iteration it: P waves on tile it (S, P, dV), dS waves one tile behind
     // (dP, dS, dK); every LDS operand of a tile is read ahead of its products.
+    // q0: first row of the wave's tile (a compute cursor, one step per tile).
     const unsigned slab0 = lbase + NSK * STAGE_DKDV + kwave * PSLAB;
     int st_p = 0, st_ds = NSK - 1;
+    int q0 = row_first;
+    const bool keys_live = wkey0 < G.nk;   // a key group past the last key idles
     for (int it = 0; ntiles > 0 && it <= ntiles; ++it) {
         int ns = st_p + PDK;
         if (ns >= NSK) ns -= NSK;
-        issue(it + PDK, ns);
+        issue(ns);
+        advance();
         const int u = ds_wave ? it - 1 : it;
-        const int q0 = (qstart + (u < 0 ? 0 : u) % per_head) * TR;
-        // (a key group past the last key idles)
-        if (u >= 0 && u < ntiles && wkey0 < G.nk && (!G.causal || q0 + TR - 1 >= wkey0)) {
+        if (u >= 0 && u < ntiles && keys_live && (!G.causal || q0 + TR - 1 >= wkey0)) {
             const unsigned sT = lbase + (ds_wave ? st_ds : st_p) * STAGE_DKDV;
             const unsigned lslot = sT + 2 * TB + wave * LD_SLOT;
             const unsigned slab = slab0 + (u & 1) * (KW * PSLAB);
@@ -579,13 +660,13 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
             const unsigned sA = ds_wave ? sT : sT + TB;
             bf16x8 ar[D / 16], at[2][D / 32];
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(sR + L.roff(kk));
+            for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(sR + ro[kk]);
 #pragma unroll
             for (int qc = 0; qc < 2; ++qc)
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-                    at[qc][dt] = vt_read2(sA + L.toff(dt, 0) + qc * 16 * RB,
-                                          sA + L.toff(dt, 1) + qc * 16 * RB);
+                    at[qc][dt] = vt_read2(sA + to[dt][0] + qc * 16 * RB,
+                                          sA + to[dt][1] + qc * 16 * RB);
             __builtin_amdgcn_sched_barrier(0);
             f32x16 s = {};
 #pragma unroll
@@ -656,6 +737,10 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
         lds_barrier();
         st_ds = st_p;
         st_p = st_p + 1 == NSK ? 0 : st_p + 1;
+        if (u >= 0) {
+            q0 += TR;
+            if (q0 >= row_end) q0 = row_first;
+        }
     }
     wait_vmcnt<0>();
 

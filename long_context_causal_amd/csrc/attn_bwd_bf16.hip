@@ -503,14 +503,15 @@ attn_bwd_dq_share(BwdParams p) {
 // The workgroup streams 32-row tiles of Q and dO (with L and D) for hpw
 // query heads of the group through NSK stages, PDK tiles ahead; the group's
 // heads are split over head_splits workgroups, which sum into dk, dv with
-// fp32 atomics.  Wave w copies rows 4w .. 4w+3 of Q and dO and, into a slot
-// of its own, the tile's L (lanes 0-31) and D (lanes 32-63).
+// fp32 atomics.  Only the dS waves copy (the P waves carry the exp): dS wave
+// 4 + w copies rows 8w .. 8w+7 of Q and dO and the tile's L (lanes 0-31)
+// and D (lanes 32-63) into the stage's L/D slot.
 constexpr int NWK = 8;                         // waves per dK/dV workgroup
 constexpr int KW = 4;                          // key groups of 32 per workgroup
 constexpr int NSK = 5;                         // stages: PDK ahead + the two tiles in use
 constexpr int PDK = NSK - 2;
-constexpr int LD_SLOT = 64 * 4;                // one wave's L and D of a tile
-constexpr int STAGE_DKDV = 2 * TB + NWK * LD_SLOT;   // Q, dO, L/D slots
+constexpr int LD_SLOT = 1024;                  // the tile's L and D (256 bytes used)
+constexpr int STAGE_DKDV = 2 * TB + LD_SLOT;   // Q, dO, L/D
 constexpr int PSLAB = 64 * 16 * 4;             // one key group's fp32 P of a tile
 constexpr int DKDV_LDS = NSK * STAGE_DKDV + 2 * KW * PSLAB;
 
@@ -572,65 +573,8 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
     const int nqt = (G.nq + TR - 1) / TR;
     const int per_head = max(nqt - qstart, 0);
     const int ntiles = per_head * hpw;
-    const int64_t row_bytes = (int64_t)p.hq * D * 2;
-    const int64_t row_step = TR * row_bytes;
     const int row_first = qstart * TR, row_end = nqt * TR;
-    const unsigned coff = copy_offset(lane, wave, row_bytes);
-    // Copy cursor: tile cu of the workgroup (heads in turn, rows in 32-row
-    // tiles), as byte pointers to its first row in Q and dO and the index
-    // of that row's L and D.  Tiles past the last repeat it, so every wave
-    // issues 3 copies per tile.
-    int cu = 0, cr0 = row_first;
-    const int64_t hrow0 = (int64_t)n * p.two_c + G.qrow0;   // row of the sample's query 0
-    const char *cq = (const char *)(p.q + (hrow0 * p.hq + h0) * D) + row_first * row_bytes;
-    const char *cdo = (const char *)(p.dout + (hrow0 * p.hq + h0) * D) + row_first * row_bytes;
-    int64_t cli = ((int64_t)n * p.hq + h0) * p.two_c + G.qrow0 + row_first;
-    // lanes 0-31 copy L, lanes 32-63 D (the same layout); the per-lane base
-    // is settled here so no wait for its load is left inside the tile loop
-    const float *ld_lane = (hi ? p.delta : p.lse) + l32;
-    settle(ld_lane);
-    auto issue = [&](int stage) {
-        const unsigned sb = lbase + stage * STAGE_DKDV;
-        const unsigned sld = sb + 2 * TB + wave * LD_SLOT;
-        if (cr0 + TR <= G.nq) {
-            dma16(cq + 4 * wave * row_bytes, coff, sb + wave * 1024);
-            dma16(cdo + 4 * wave * row_bytes, coff, sb + TB + wave * 1024);
-            dma4(ld_lane + cli, sld);
-        } else {
-            // the last tile of a head crosses the sample's last row: rows
-            // past it repeat it
-            const int64_t back = (int64_t)cr0 * row_bytes;
-            copy_rows((const uint16_t *)(cq - back), row_bytes, cr0, G.nq, wave, coff, sb, lane);
-            copy_rows((const uint16_t *)(cdo - back), row_bytes, cr0, G.nq, wave, coff, sb + TB,
-                      lane);
-            dma4(ld_lane - l32 + (cli - cr0) + min(cr0 + l32, G.nq - 1), sld);
-        }
-    };
-    auto advance = [&]() {
-        if (cu + 1 >= ntiles) return;
-        ++cu;
-        cr0 += TR;
-        cq += row_step;
-        cdo += row_step;
-        cli += TR;
-        if (cr0 >= row_end) {   // next head
-            const int64_t rows = row_end - row_first;
-            cr0 = row_first;
-            cq += 2 * D - rows * row_bytes;
-            cdo += 2 * D - rows * row_bytes;
-            cli += p.two_c - rows;
-        }
-    };
-    if (ntiles > 0) {
-#pragma unroll
-        for (int i = 0; i < PDK; ++i) {
-            issue(i);
-            advance();
-        }
-        wait_vmcnt<3 * (PDK - 1)>();
-    }
-    lds_barrier();
-    // The lane's LDS read offsets in a tile (the stage base is added per read).
+    // the lane's LDS read offsets in a tile (the stage base is added per read)
     unsigned ro[D / 16], to[D / 32][2];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) ro[kk] = L.roff(kk);
@@ -639,41 +583,39 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
         to[dt][0] = L.toff(dt, 0);
         to[dt][1] = L.toff(dt, 1);
     }
-    // Iteration it: P waves on tile it (S, P, dV), dS waves one tile behind
-    // (dP, dS, dK); every LDS operand of a tile is read ahead of its products.
-    // q0: first row of the wave's tile (a compute cursor, one step per tile).
     const unsigned slab0 = lbase + NSK * STAGE_DKDV + kwave * PSLAB;
-    int st_p = 0, st_ds = NSK - 1;
-    int q0 = row_first;
     const bool keys_live = wkey0 < G.nk;   // a key group past the last key idles
-    for (int it = 0; ntiles > 0 && it <= ntiles; ++it) {
-        int ns = st_p + PDK;
-        if (ns >= NSK) ns -= NSK;
-        issue(ns);
-        advance();
-        const int u = ds_wave ? it - 1 : it;
-        if (u >= 0 && u < ntiles && keys_live && (!G.causal || q0 + TR - 1 >= wkey0)) {
-            const unsigned sT = lbase + (ds_wave ? st_ds : st_p) * STAGE_DKDV;
-            const unsigned lslot = sT + 2 * TB + wave * LD_SLOT;
-            const unsigned slab = slab0 + (u & 1) * (KW * PSLAB);
-            const unsigned sR = ds_wave ? sT + TB : sT;
-            const unsigned sA = ds_wave ? sT : sT + TB;
-            bf16x8 ar[D / 16], at[2][D / 32];
+    // q0: first row of a wave's tile (a compute cursor, one step per tile)
+    auto visible = [&](int q0) { return keys_live && (!G.causal || q0 + TR - 1 >= wkey0); };
+    auto next_row = [&](int &q0) {
+        q0 += TR;
+        if (q0 >= row_end) q0 = row_first;
+    };
+
+    if (!ds_wave) {
+        // P wave, iteration it: tile it (S, P, dV); no copies.
+        lds_barrier();
+        int st = 0, q0 = row_first;
+        for (int it = 0; ntiles > 0 && it <= ntiles; ++it) {
+            if (it < ntiles && visible(q0)) {
+                const unsigned sT = lbase + st * STAGE_DKDV;
+                const unsigned lslot = sT + 2 * TB;
+                const unsigned slab = slab0 + (it & 1) * (KW * PSLAB);
+                // every LDS operand of the tile is read ahead of its products
+                bf16x8 ar[D / 16], at[2][D / 32];
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(sR + ro[kk]);
+                for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(sT + ro[kk]);
 #pragma unroll
-            for (int qc = 0; qc < 2; ++qc)
+                for (int qc = 0; qc < 2; ++qc)
 #pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    at[qc][dt] = vt_read2(sA + to[dt][0] + qc * 16 * RB,
-                                          sA + to[dt][1] + qc * 16 * RB);
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 s = {};
+                    for (int dt = 0; dt < D / 32; ++dt)
+                        at[qc][dt] = vt_read2(sT + TB + to[dt][0] + qc * 16 * RB,
+                                              sT + TB + to[dt][1] + qc * 16 * RB);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x16 s = {};
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) s = MFMA(ar[kk], bf[kk], s, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 ob[2];
-            if (!ds_wave) {
+                for (int kk = 0; kk < D / 16; ++kk) s = MFMA(ar[kk], bf[kk], s, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
                 const bool full = q0 + TR <= G.nq && wkey0 + TR <= G.nk &&
                                   (!G.causal || wkey0 + TR - 1 <= q0);
                 f32x16 x;
@@ -701,6 +643,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                     *(__attribute__((address_space(3))) f32x4 *)(uintptr_t)(
                         slab + (j * 64 + lane) * 16) =
                         f32x4{pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]};
+                bf16x8 ob[2];
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc) {
                     f32x8 h;
@@ -708,7 +651,108 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                     for (int e = 0; e < 8; ++e) h[e] = pv[qc * 8 + e];
                     ob[qc] = __builtin_convertvector(h, bf16x8);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+                        acc[dt] = MFMA(at[qc][dt], ob[qc], acc[dt], 0, 0, 0);
+            }
+            lds_barrier();   // (the dS waves have waited for tile it + 1)
+            st = st + 1 == NSK ? 0 : st + 1;
+            if (it < ntiles) next_row(q0);
+        }
+    } else {
+        // dS wave, iteration it: copies tile it + PDK, computes tile it - 1
+        // (dP, dS, dK) with the P the P wave handed over.
+        const int cw = kwave;   // copies rows 8 cw .. 8 cw + 7 of Q and dO
+        const int64_t row_bytes = (int64_t)p.hq * D * 2;
+        const int64_t row_step = TR * row_bytes;
+        const unsigned coff0 = copy_offset(lane, 2 * cw, row_bytes);
+        const unsigned coff1 = copy_offset(lane, 2 * cw + 1, row_bytes);
+        // Copy cursor: tile cu of the workgroup (heads in turn, rows in
+        // 32-row tiles), as byte pointers to its first row in Q and dO and
+        // the index of that row's L and D.  Tiles past the last repeat it,
+        // so every dS wave issues 5 copies per tile.
+        int cu = 0, cr0 = row_first;
+        const int64_t hrow0 = (int64_t)n * p.two_c + G.qrow0;   // row of the sample's query 0
+        const char *cq = (const char *)(p.q + (hrow0 * p.hq + h0) * D) + row_first * row_bytes;
+        const char *cdo = (const char *)(p.dout + (hrow0 * p.hq + h0) * D) + row_first * row_bytes;
+        int64_t cli = ((int64_t)n * p.hq + h0) * p.two_c + G.qrow0 + row_first;
+        // the L/D slot: lanes 0-31 copy L, lanes 32-63 D (the same layout);
+        // the four dS waves write the same bytes.  The per-lane base is
+        // settled here so no wait for its load is left inside the tile loop.
+        const float *ld_lane = (hi ? p.delta : p.lse) + l32;
+        settle(ld_lane);
+        auto issue = [&](int stage) {
+            const unsigned sb = lbase + stage * STAGE_DKDV;
+            if (cr0 + TR <= G.nq) {
+                dma16(cq + 8 * cw * row_bytes, coff0, sb + 2 * cw * 1024);
+                dma16(cq + (8 * cw + 4) * row_bytes, coff1, sb + (2 * cw + 1) * 1024);
+                dma16(cdo + 8 * cw * row_bytes, coff0, sb + TB + 2 * cw * 1024);
+                dma16(cdo + (8 * cw + 4) * row_bytes, coff1, sb + TB + (2 * cw + 1) * 1024);
+                dma4(ld_lane + cli, sb + 2 * TB);
             } else {
+                // the last tile of a head crosses the sample's last row: rows
+                // past it repeat it
+                const int64_t back = (int64_t)cr0 * row_bytes;
+                const uint16_t *qb = (const uint16_t *)(cq - back);
+                const uint16_t *db = (const uint16_t *)(cdo - back);
+                copy_rows(qb, row_bytes, cr0, G.nq, 2 * cw, coff0, sb, lane);
+                copy_rows(qb, row_bytes, cr0, G.nq, 2 * cw + 1, coff1, sb, lane);
+                copy_rows(db, row_bytes, cr0, G.nq, 2 * cw, coff0, sb + TB, lane);
+                copy_rows(db, row_bytes, cr0, G.nq, 2 * cw + 1, coff1, sb + TB, lane);
+                dma4(ld_lane - l32 + (cli - cr0) + min(cr0 + l32, G.nq - 1), sb + 2 * TB);
+            }
+        };
+        auto advance = [&]() {
+            if (cu + 1 >= ntiles) return;
+            ++cu;
+            cr0 += TR;
+            cq += row_step;
+            cdo += row_step;
+            cli += TR;
+            if (cr0 >= row_end) {   // next head
+                const int64_t rows = row_end - row_first;
+                cr0 = row_first;
+                cq += 2 * D - rows * row_bytes;
+                cdo += 2 * D - rows * row_bytes;
+                cli += p.two_c - rows;
+            }
+        };
+        if (ntiles > 0) {
+#pragma unroll
+            for (int i = 0; i < PDK; ++i) {
+                issue(i);
+                advance();
+            }
+            wait_vmcnt<5 * (PDK - 1)>();
+        }
+        lds_barrier();
+        int st = NSK - 1, cst = PDK, q0 = row_first;
+        for (int it = 0; ntiles > 0 && it <= ntiles; ++it) {
+            issue(cst);
+            advance();
+            cst = cst + 1 == NSK ? 0 : cst + 1;
+            if (it > 0 && visible(q0)) {
+                const unsigned sT = lbase + st * STAGE_DKDV;
+                const unsigned lslot = sT + 2 * TB;
+                const unsigned slab = slab0 + ((it - 1) & 1) * (KW * PSLAB);
+                bf16x8 ar[D / 16], at[2][D / 32];
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(sT + TB + ro[kk]);
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+                        at[qc][dt] = vt_read2(sT + to[dt][0] + qc * 16 * RB,
+                                              sT + to[dt][1] + qc * 16 * RB);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x16 s = {};
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) s = MFMA(ar[kk], bf[kk], s, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                bf16x8 ob[2];
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc) {
                     const f32x8 dv8 = *(const __attribute__((address_space(3))) f32x8 *)(
@@ -725,24 +769,20 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                     }
                     ob[qc] = __builtin_convertvector(ds, bf16x8);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+                    for (int dt = 0; dt < D / 32; ++dt)
+                        acc[dt] = MFMA(at[qc][dt], ob[qc], acc[dt], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int qc = 0; qc < 2; ++qc)
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-                    acc[dt] = MFMA(at[qc][dt], ob[qc], acc[dt], 0, 0, 0);
+            wait_vmcnt<5 * (PDK - 1)>();   // tile it + 1 has landed
+            lds_barrier();
+            st = st + 1 == NSK ? 0 : st + 1;
+            if (it > 0) next_row(q0);
         }
-        wait_vmcnt<3 * (PDK - 1)>();   // tile it + 1 has landed
-        lds_barrier();
-        st_ds = st_p;
-        st_p = st_p + 1 == NSK ? 0 : st_p + 1;
-        if (u >= 0) {
-            q0 += TR;
-            if (q0 >= row_end) q0 = row_first;
-        }
+        wait_vmcnt<0>();
     }
-    wait_vmcnt<0>();
 
     // dv += dV (P waves), dk += scale dK (dS waves); lane holds head dims
     // dt*32 + 8*i + 4*hi + j.  Split heads add with atomics.

@@ -286,8 +286,10 @@ int cpattn_step_bwd(const cpattn_dims *dims, int dtype, float scale, int mode,
                     float *dq_r, float *dk_src, float *dv_src, void *stream);
 
 /* cpattn_backward, device: one rank's whole backward share.  Zeroes dkz
- * and dvz [cp, b, 2c, hkv, d] (fp32), computes delta into delta_ws
- * [b, hq, 2c] (caller's workspace), then the cp steps of cpattn_step_mode:
+ * and dvz [cp, b, 2c, hkv, d] (fp32), writes -L/scale and -D (D as in
+ * cpattn_bwd_delta) of the rank's rows into delta_ws [2, b, hq, 2c] (the
+ * caller's fp32 workspace; the two per-row terms the kernels start the sums
+ * of S and dP from), then the cp steps of cpattn_step_mode:
  * dq_r [b, 2c, hq, d] (fp32) is written with the sum over all steps (every
  * row; its previous contents are ignored), and step i adds to rank src's
  * slices of dkz/dvz.  dkz/dvz

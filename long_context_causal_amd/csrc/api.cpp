@@ -527,14 +527,6 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
     const int64_t q_elems = dims->b * two_c * dims->hq * dims->d;
     const int64_t kv_elems = dims->b * two_c * dims->hkv * dims->d;
     const char *q_r = (const char *)qz + rank * q_elems * 2;
-    hipError_t e = cpattn::launch_fill_zero(dkz, kv_elems * dims->cp, s);
-    if (e == hipSuccess) e = cpattn::launch_fill_zero(dvz, kv_elems * dims->cp, s);
-    if (e == hipSuccess) e = cpattn::launch_bwd_delta(dims->b, two_c, dims->hq, o_r, do_r,
-                                                      delta_ws, s);
-    if (e != hipSuccess) return CPATTN_EHIP;
-    // every step's dq in one grid (a workgroup streams all steps' keys for
-    // its query rows and writes dq once), then every step's dK/dV in one
-    // grid (each step owns its source block's contribution)
     const int cp = dims->cp;
     std::vector<StepGeom> geo(cp);
     std::vector<int> modes(cp);
@@ -553,12 +545,24 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
         dks[i] = dkz + src * kv_elems;
         dvs[i] = dvz + src * kv_elems;
     }
-    e = cpattn::launch_bwd_dq_share_bf16(geo[0], t, rank, cp, q_r, kz, vz, do_r, lse_r,
-                                         delta_ws, dq_r, s);
+    // the workspace: -L/scale and -D of the rank's rows, the terms the
+    // grids start S and dP from
+    float *nl = delta_ws, *nd = delta_ws + dims->b * dims->hq * two_c;
+    const float inv_scale = (float)(1.0 / (double)geo[0].scale);
+    hipError_t e = cpattn::launch_fill_zero(dkz, kv_elems * dims->cp, s);
+    if (e == hipSuccess) e = cpattn::launch_fill_zero(dvz, kv_elems * dims->cp, s);
+    if (e == hipSuccess)
+        e = cpattn::launch_bwd_prep(dims->b, two_c, dims->hq, o_r, do_r, lse_r, inv_scale, nl,
+                                    nd, s);
+    if (e != hipSuccess) return CPATTN_EHIP;
+    // every step's dq in one grid (a workgroup streams all steps' keys for
+    // its query rows and writes dq once), then every step's dK/dV in one
+    // grid (each step owns its source block's contribution)
+    e = cpattn::launch_bwd_dq_share_bf16(geo[0], t, rank, cp, q_r, kz, vz, do_r, nl, nd, dq_r,
+                                         s);
     if (e != hipSuccess) return CPATTN_EHIP;
     e = cpattn::launch_bwd_dkdv_steps_bf16(cp, geo.data(), t, modes.data(), q_r, ks.data(),
-                                           vs.data(), do_r, lse_r, delta_ws, dks.data(),
-                                           dvs.data(), s);
+                                           vs.data(), do_r, nl, nd, dks.data(), dvs.data(), s);
     if (e != hipSuccess) return CPATTN_EHIP;
     return CPATTN_OK;
 }

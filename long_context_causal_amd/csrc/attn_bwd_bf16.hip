@@ -161,6 +161,13 @@ __device__ __forceinline__ void settle(const T (&x)[N]) {
     for (int i = 0; i < N; ++i) settle(x[i]);
 }
 
+// x as computed, held in a VGPR: a constant added to it afterwards goes into
+// the LDS instruction's offset field instead of a new add of the stage base.
+__device__ __forceinline__ unsigned pin(unsigned x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 #define MFMA __builtin_amdgcn_mfma_f32_32x32x16_bf16
 
 // Issues one wave's copies of rows [4 m, 4 m + 4) of a 32-row tile whose
@@ -283,7 +290,9 @@ struct DqSharePlan {
     }
 };
 
-template <class Plan, bool ACCUMULATE>
+// PREP: p.lse and p.delta hold -L/scale and -D (launch_bwd_prep) instead
+// of L and D.
+template <class Plan, bool ACCUMULATE, bool PREP>
 __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -324,8 +333,8 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
     load_b_rows(p.q + qoff, hi, qf);
     load_b_rows(p.dout + qoff, hi, df);
     const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + P.qrow0 + qr;
-    const float lq = p.lse[lrow] * LOG2E;
-    const float dq_d = p.delta[lrow];
+    const float lq = PREP ? -p.lse[lrow] * p.scale_log2 : p.lse[lrow] * LOG2E;
+    const float dq_d = PREP ? -p.delta[lrow] : p.delta[lrow];
     settle(qf);
     settle(df);
     settle(lq);
@@ -397,14 +406,15 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
                                         (T.see == SEE_SECOND ? wrow0 + TR - 1 >= c_half
                                                              : T.key0 <= wrow0));
         if (comp) {
-            const unsigned sK = lbase + stage * STAGE_DQ, sV = sK + TB;
+            const unsigned sK = lbase + stage * STAGE_DQ;
             // the tile's LDS operands are read ahead of the products
             // (the transposed K^T reads go out behind the S, dP products)
             bf16x8 ak[D / 16], av[D / 16], at[2][D / 32];
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk) {
-                ak[kk] = k_read(sK + ro[kk]);
-                av[kk] = k_read(sV + ro[kk]);
+                const unsigned a = pin(sK + ro[kk]);
+                ak[kk] = k_read(a);
+                av[kk] = k_read(a + TB);
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x16 s = {}, dp = {};
@@ -414,12 +424,17 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
                 dp = MFMA(av[kk], df[kk], dp, 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
+            unsigned ta[D / 32][2];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                ta[dt][0] = pin(sK + to[dt][0]);
+                ta[dt][1] = pin(sK + to[dt][1]);
+            }
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
-                    at[kc][dt] = vt_read2(sK + to[dt][0] + kc * 16 * RB,
-                                          sK + to[dt][1] + kc * 16 * RB);
+                    at[kc][dt] = vt_read2(ta[dt][0] + kc * 16 * RB, ta[dt][1] + kc * 16 * RB);
             __builtin_amdgcn_sched_barrier(0);
             const int key0 = T.key0;
             // tile entirely visible to the wave's rows: no mask
@@ -481,7 +496,7 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
 __global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
-    dq_body<DqStepPlan, true>(p, lds);
+    dq_body<DqStepPlan, true, false>(p, lds);
 }
 
 // The dq of all cp steps of a rank's share in one grid: a workgroup streams
@@ -489,7 +504,7 @@ attn_bwd_dq(BwdParams p) {
 __global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_share(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
-    dq_body<DqSharePlan, false>(p, lds);
+    dq_body<DqSharePlan, false, true>(p, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -527,6 +542,10 @@ struct KvStep {
 
 // The dK/dV workgroup 'item' of one step (item as blockIdx.x of that
 // step's own launch).
+// PREP: p.lse and p.delta hold -L/scale and -D (launch_bwd_prep): they
+// start the sums of S and dP, so that S already holds q.k - L/scale and dP
+// holds dO.v - D.
+template <bool PREP>
 __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, int item,
                                           char *lds) {
     const int tid = threadIdx.x, lane = tid & 63;
@@ -604,15 +623,30 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                 // every LDS operand of the tile is read ahead of its products
                 bf16x8 ar[D / 16], at[2][D / 32];
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(sT + ro[kk]);
+                for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(pin(sT + ro[kk]));
+                unsigned ta[D / 32][2];
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    ta[dt][0] = pin(sT + TB + to[dt][0]);
+                    ta[dt][1] = pin(sT + TB + to[dt][1]);
+                }
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc)
 #pragma unroll
                     for (int dt = 0; dt < D / 32; ++dt)
-                        at[qc][dt] = vt_read2(sT + TB + to[dt][0] + qc * 16 * RB,
-                                              sT + TB + to[dt][1] + qc * 16 * RB);
+                        at[qc][dt] = vt_read2(ta[dt][0] + qc * 16 * RB, ta[dt][1] + qc * 16 * RB);
+                // the L terms of the lane's 16 rows
+                f32x16 lv;
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc) {
+                    const f32x8 h = *(const __attribute__((address_space(3))) f32x8 *)(
+                        uintptr_t)(lslot + (16 * qc + 8 * hi) * 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) lv[qc * 8 + e] = h[e];
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 f32x16 s = {};
+                if (PREP) s = lv;   // -L/scale
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) s = MFMA(ar[kk], bf[kk], s, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
@@ -620,13 +654,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                                   (!G.causal || wkey0 + TR - 1 <= q0);
                 f32x16 x;
 #pragma unroll
-                for (int qc = 0; qc < 2; ++qc) {
-                    const f32x8 lv = *(const __attribute__((address_space(3))) f32x8 *)(
-                        uintptr_t)(lslot + (16 * qc + 8 * hi) * 4);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        x[qc * 8 + e] = __builtin_fmaf(s[qc * 8 + e], p.scale_log2, -LOG2E * lv[e]);
-                }
+                for (int i = 0; i < 16; ++i)
+                    x[i] = PREP ? s[i] * p.scale_log2
+                                : __builtin_fmaf(s[i], p.scale_log2, -LOG2E * lv[i]);
                 if (!full) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
@@ -740,23 +770,36 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                 const unsigned slab = slab0 + ((it - 1) & 1) * (KW * PSLAB);
                 bf16x8 ar[D / 16], at[2][D / 32];
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(sT + TB + ro[kk]);
+                for (int kk = 0; kk < D / 16; ++kk) ar[kk] = k_read(pin(sT + TB + ro[kk]));
+                unsigned ta[D / 32][2];
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt) {
+                    ta[dt][0] = pin(sT + to[dt][0]);
+                    ta[dt][1] = pin(sT + to[dt][1]);
+                }
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc)
 #pragma unroll
                     for (int dt = 0; dt < D / 32; ++dt)
-                        at[qc][dt] = vt_read2(sT + to[dt][0] + qc * 16 * RB,
-                                              sT + to[dt][1] + qc * 16 * RB);
+                        at[qc][dt] = vt_read2(ta[dt][0] + qc * 16 * RB, ta[dt][1] + qc * 16 * RB);
+                // the D terms of the lane's 16 rows
+                f32x16 dv;
+#pragma unroll
+                for (int qc = 0; qc < 2; ++qc) {
+                    const f32x8 h = *(const __attribute__((address_space(3))) f32x8 *)(
+                        uintptr_t)(lslot + TR * 4 + (16 * qc + 8 * hi) * 4);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dv[qc * 8 + e] = h[e];
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 f32x16 s = {};
+                if (PREP) s = dv;   // -D
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) s = MFMA(ar[kk], bf[kk], s, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 bf16x8 ob[2];
 #pragma unroll
                 for (int qc = 0; qc < 2; ++qc) {
-                    const f32x8 dv8 = *(const __attribute__((address_space(3))) f32x8 *)(
-                        uintptr_t)(lslot + TR * 4 + (16 * qc + 8 * hi) * 4);
                     const f32x4 pa = *(const __attribute__((address_space(3))) f32x4 *)(
                         uintptr_t)(slab + ((2 * qc) * 64 + lane) * 16);
                     const f32x4 pb = *(const __attribute__((address_space(3))) f32x4 *)(
@@ -764,8 +807,9 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                     f32x8 ds;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        ds[e] = pa[e] * (s[qc * 8 + e] - dv8[e]);
-                        ds[4 + e] = pb[e] * (s[qc * 8 + 4 + e] - dv8[4 + e]);
+                        const int i = qc * 8 + e;
+                        ds[e] = pa[e] * (PREP ? s[i] : s[i] - dv[i]);
+                        ds[4 + e] = pb[e] * (PREP ? s[i + 4] : s[i + 4] - dv[i + 4]);
                     }
                     ob[qc] = __builtin_convertvector(ds, bf16x8);
                 }
@@ -816,7 +860,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
 __global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
-    dkdv_item(p, KvStep{p.k, p.v, p.dk, p.dv, p.mode, p.head_splits, p.tab.tile0}, blockIdx.x,
+    dkdv_item<false>(p, KvStep{p.k, p.v, p.dk, p.dv, p.mode, p.head_splits, p.tab.tile0}, blockIdx.x,
               lds);
 }
 
@@ -849,7 +893,7 @@ attn_bwd_dkdv_steps(DkdvStepsParams sp) {
     int j = 0;
     while (j + 1 < sp.nsteps && sp.st[j + 1].item0 <= item) ++j;
     const KvStepDesc &d = sp.st[j];
-    dkdv_item(sp.p,
+    dkdv_item<true>(sp.p,
               KvStep{d.k, d.v, d.dk, d.dv, d.mode, 1,
                      d.mode == CPATTN_KV_FIRST_HALF ? sp.tile0_half : sp.p.tab.tile0},
               item - d.item0, lds);
@@ -857,9 +901,13 @@ attn_bwd_dkdv_steps(DkdvStepsParams sp) {
 
 // ---------------------------------------------------------------------------
 // D[n, h, i] = sum_t dO[n, i, h, t] O[n, i, h, t]: one thread per (n, i, h).
+// PREP: writes -D, and -L[n, h, i] * inv_scale to nl (the terms the share's
+// backward grids start S and dP from).
+template <bool PREP>
 __global__ void __launch_bounds__(256) bwd_delta(const float *o, const uint16_t *dout,
                                                  float *delta, int64_t rows, int hq,
-                                                 int64_t two_c) {
+                                                 int64_t two_c, const float *lse,
+                                                 float inv_scale, float *nl) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (n*2c + i)*hq + h
     if (idx >= rows) return;
     const float *orow = o + idx * D;
@@ -878,7 +926,13 @@ __global__ void __launch_bounds__(256) bwd_delta(const float *o, const uint16_t 
     const int h = (int)(idx % hq);
     const int64_t ni = idx / hq;
     const int64_t i = ni % two_c, n = ni / two_c;
-    delta[(n * hq + h) * two_c + i] = acc;
+    const int64_t out = (n * hq + h) * two_c + i;
+    if (PREP) {
+        delta[out] = -acc;
+        nl[out] = -lse[out] * inv_scale;
+    } else {
+        delta[out] = acc;
+    }
 }
 
 // x[0 .. n) = 0, 16 bytes per thread (n a multiple of 4).
@@ -893,8 +947,20 @@ hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o, co
                             float *delta, hipStream_t stream) {
     const int64_t rows = b * two_c * hq;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_delta, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, o,
-                       (const uint16_t *)dout, delta, rows, hq, two_c);
+    hipLaunchKernelGGL(bwd_delta<false>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       stream, o, (const uint16_t *)dout, delta, rows, hq, two_c, nullptr, 0.0f,
+                       nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, const float *o, const void *dout,
+                           const float *lse, float inv_scale, float *nl, float *nd,
+                           hipStream_t stream) {
+    const int64_t rows = b * two_c * hq;
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_delta<true>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       stream, o, (const uint16_t *)dout, nd, rows, hq, two_c, lse, inv_scale,
+                       nl);
     return hipGetLastError();
 }
 

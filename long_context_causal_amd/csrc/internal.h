@@ -93,24 +93,30 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
                                 float *dv, hipStream_t stream, bool with_dkdv = true);
 // The dq of all cp steps of rank's share in one grid (bf16): kz, vz are the
 // partitioned K, V of all ranks; every row of dq is written (not added to).
+// nl, nd: -L/scale and -D of the rank's rows (launch_bwd_prep).
 hipError_t launch_bwd_dq_share_bf16(const StepGeom &g, const SeqTable &tab, int rank, int cp,
                                     const void *q, const void *kz, const void *vz,
-                                    const void *dout, const float *lse, const float *delta,
+                                    const void *dout, const float *nl, const float *nd,
                                     float *dq, hipStream_t stream);
 // The dK/dV of steps 0 .. n-1 of one rank's share in one grid: step i
 // reads k[i]/v[i] and adds to dk[i]/dv[i] (distinct blocks, zeroed by the
 // caller), mode[i] its mode; g[0] supplies the dims and scale, tab the
-// packed samples.
+// packed samples; nl, nd as for the dq grid.
 hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &tab,
                                       const int *mode,
                                       const void *q, const void *const *k,
                                       const void *const *v, const void *dout,
-                                      const float *lse, const float *delta, float *const *dk,
+                                      const float *nl, const float *nd, float *const *dk,
                                       float *const *dv, hipStream_t stream);
 
 // delta[n, h, i] = sum_t dout[n, i, h, t] o[n, i, h, t]; o fp32, dout bf16.
 hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o,
                             const void *dout, float *delta, hipStream_t stream);
+// The per-row terms the share's backward grids start their sums from:
+// nl[n, h, i] = -lse[n, h, i] * inv_scale and nd[n, h, i] = -delta[n, h, i].
+hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, const float *o, const void *dout,
+                           const float *lse, float inv_scale, float *nl, float *nd,
+                           hipStream_t stream);
 
 // x[0 .. n) = 0 (n a multiple of 4, x 16-byte aligned).
 hipError_t launch_fill_zero(float *x, int64_t n, hipStream_t stream);

@@ -154,7 +154,7 @@ class CPProblem:
         two_c = 2 * self.c
         f = dict(dtype=torch.float32, device=self.device)
         return dict(rank=rank,
-                    delta=torch.empty((self.b, self.w.hq, two_c), **f),
+                    delta=torch.empty((2, self.b, self.w.hq, two_c), **f),
                     dq=torch.empty((self.b, two_c, self.w.hq, self.w.d), **f),
                     dkz=torch.empty((self.cp, self.b, two_c, self.w.hkv, self.w.d), **f),
                     dvz=torch.empty((self.cp, self.b, two_c, self.w.hkv, self.w.d), **f))

@@ -122,6 +122,14 @@ hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o, co
     return hipSuccess;
 }
 
+hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, const float *o, const void *dout,
+                           const float *lse, float inv_scale, float *nl, float *nd, hipStream_t) {
+    REQUIRE(b >= 1 && two_c >= 2 && hq >= 1 && o && dout && lse && nl && nd);
+    REQUIRE(inv_scale > 0.0f && nd == nl + b * hq * two_c);
+    ++stubs::launches[stubs::DELTA];
+    return hipSuccess;
+}
+
 hipError_t launch_fill_zero(float *x, int64_t n, hipStream_t) {
     REQUIRE(x && n >= 0 && n % 4 == 0);
     ++stubs::launches[stubs::FILL];

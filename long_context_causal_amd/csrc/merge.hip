@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, i
                                                  int64_t two_c, int hq, int d,
                                                  const float *run_o, const float *run_l,
                                                  void *o_out, float *lse_out) {
-    __shared__ float w[MAX_LDS_WEIGHTS];   // [heads of the run][n_cover]: L_p, then weights
+    __shared__ float w[MAX_LDS_WEIGHTS];   // [n_cover][heads of the run]: L_p, then weights
     __shared__ const float *obase[NP + 1]; // covering partial c: its O at (n, row, head 0)
     __shared__ const float *lbase[NP + 1]; // its L at (n, head 0, row)
     __shared__ int lstride[NP + 1];        // its L elements between heads (its rows)
@@ -87,7 +87,8 @@ __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, i
     const int nc = n_cover;
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr float LN2 = 0.69314718055994531f;
-    const int vec_per_head = d / 4;
+    const int vec_per_head = d / 4;                      // 16 or 32
+    const int vph_shift = __builtin_ctz(vec_per_head);
     const int64_t nvec_row = (int64_t)hq * vec_per_head;
     auto store = [&](int i, const f32x4 &a) {
         if (BF16_OUT) {
@@ -124,23 +125,30 @@ __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, i
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int e = e0 + k * NT + threadIdx.x;
-                if (e < ne) w[e] = lv[k];
+                if (e < ne) {
+                    const int h = e / nc, c = e - h * nc;
+                    w[c * nh + h] = lv[k];
+                }
             }
         }
         __syncthreads();
+        // one lane per head; partial c of head h at w[c * nh + h], so the
+        // lanes of a wave read consecutive words
         for (int h = threadIdx.x; h < nh; h += NT) {
-            float *wh = w + h * nc;
+            float *wh = w + h;
             float mx = -INFINITY;
-            for (int c = 0; c < nc; ++c) mx = fmaxf(mx, wh[c]);
+            for (int c = 0; c < nc; ++c) mx = fmaxf(mx, wh[c * nh]);
             float total = -INFINITY;
             if (mx != -INFINITY) {
                 float ssum = 0.0f;
-                for (int c = 0; c < nc; ++c) ssum += __builtin_amdgcn_exp2f((wh[c] - mx) * LOG2E);
+                for (int c = 0; c < nc; ++c)
+                    ssum += __builtin_amdgcn_exp2f((wh[c * nh] - mx) * LOG2E);
                 total = mx + __builtin_amdgcn_logf(ssum) * LN2;
             }
             for (int c = 0; c < nc; ++c)
-                wh[c] = (total == -INFINITY) ? 0.0f
-                                             : __builtin_amdgcn_exp2f((wh[c] - total) * LOG2E);
+                wh[c * nh] = (total == -INFINITY)
+                                 ? 0.0f
+                                 : __builtin_amdgcn_exp2f((wh[c * nh] - total) * LOG2E);
             if (lse_out != nullptr) lse_out[(n * hq + h0 + h) * two_c + j] = total;
         }
         __syncthreads();
@@ -155,8 +163,12 @@ __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, i
         const int full = nvec / (KV * NT) * (KV * NT);
         for (int v0 = v_begin; v0 < v_begin + full; v0 += KV * NT) {
             f32x4 acc[KV];
+            int hk[KV];   // the vector's head in the run
 #pragma unroll
-            for (int k = 0; k < KV; ++k) acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int k = 0; k < KV; ++k) {
+                acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                hk[k] = (v0 - v_begin + k * NT + (int)threadIdx.x) >> vph_shift;
+            }
             // two partials per round trip: 2 * KV reads in flight per lane
             int c = 0;
             for (; c + 1 < nc; c += 2) {
@@ -169,8 +181,8 @@ __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, i
                 for (int k = 0; k < KV; ++k) x1[k] = s1[k * NT];
 #pragma unroll
                 for (int k = 0; k < KV; ++k) {
-                    const int wi = ((v0 - v_begin + k * NT + threadIdx.x) / vec_per_head) * nc + c;
-                    acc[k] += w[wi] * x0[k] + w[wi + 1] * x1[k];
+                    const int wi = c * nh + hk[k];
+                    acc[k] += w[wi] * x0[k] + w[wi + nh] * x1[k];
                 }
             }
             if (c < nc) {
@@ -179,18 +191,15 @@ __global__ void __launch_bounds__(NT) merge_rows(PartList<NP> pl, int n_parts, i
 #pragma unroll
                 for (int k = 0; k < KV; ++k) x0[k] = s0[k * NT];
 #pragma unroll
-                for (int k = 0; k < KV; ++k) {
-                    const int wi = ((v0 - v_begin + k * NT + threadIdx.x) / vec_per_head) * nc + c;
-                    acc[k] += w[wi] * x0[k];
-                }
+                for (int k = 0; k < KV; ++k) acc[k] += w[c * nh + hk[k]] * x0[k];
             }
 #pragma unroll
             for (int k = 0; k < KV; ++k) store(v0 + k * NT + threadIdx.x, acc[k]);
         }
         for (int i = v_begin + full + threadIdx.x; i < v_begin + nvec; i += NT) {
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            for (int c = 0; c < nc; ++c)
-                acc += w[((i - v_begin) / vec_per_head) * nc + c] * ((const f32x4 *)obase[c])[i];
+            const int hv = (i - v_begin) >> vph_shift;
+            for (int c = 0; c < nc; ++c) acc += w[c * nh + hv] * ((const f32x4 *)obase[c])[i];
             store(i, acc);
         }
         __syncthreads();   // the next run overwrites w

@@ -74,3 +74,18 @@ def test_merge_bf16_output_rounding():
     err = np.abs(o - o_ref)
     assert np.all(err <= np.abs(o_ref) * 2.0 ** -8 + 1e-5)
     assert_close("L", l, l_ref, 1e-5)
+
+
+def test_merge_heads_in_several_runs():
+    """More (head, partial) weights than the kernel's LDS holds at once: the
+    heads are merged in runs (208 heads x 40 covering partials)."""
+    b, c, hq, d = 1, 16, 208, 64
+    two_c = 2 * c
+    spans = [(0, two_c) if i % 4 else (c, c) for i in range(40)]
+    say("merge 208 heads x 40 partials")
+    parts = _partials(7, b, two_c, hq, d, spans, 5.0)
+    o, l = _gpu_merge(parts, b, two_c, hq, d, C.CPATTN_F32)
+    o_ref, l_ref = ocp.merge_outputs([(p[0].astype(np.float64), p[1].astype(np.float64), p[2])
+                                      for p in parts], two_c)
+    assert_close("O", o, o_ref, 1e-5)
+    assert_close("L", l, l_ref, 1e-5)

@@ -28,6 +28,7 @@ sample of the same rank share (every k-th local row, all heads).
 import argparse
 import dataclasses
 import json
+import re
 import os
 import sys
 import time
@@ -317,17 +318,6 @@ def _csv_rows(directory, suffix):
     return rows
 
 
-def steps_grid_lanes(w, rank):
-    """Grid size (lanes) of the rank's steps grid: 256-row query tiles of
-    every step x hq x b workgroups of 512 lanes."""
-    c = w.c
-    tiles = 0
-    for i in range(w.cp):
-        rows = c if i > rank else 2 * c          # q_second_half steps hold c rows
-        tiles += (rows + 255) // 256
-    return tiles * w.hq * w.b * 512
-
-
 def fused_grid_lanes(w):
     return (2 * w.c + 255) // 256 * w.hq * w.b * 512
 
@@ -353,24 +343,37 @@ def digest(prof_dir):
     mean = statistics.mean
     out_files = {}
 
-    # the fused launches of the headline share and of the 128k share have the
-    # same grid; the headline's come before the first backward dispatch, the
-    # 128k share's after the first dispatch of its steps grid (bench order)
-    def windows(rows, grid_key):
+    # Which launches belong to which share, by dispatch order (bench order):
+    # the headline's steps grids come before the first per-step launch
+    # (attn_step_bf16); the 128k RoPE share's launches come after the first
+    # partition_rope (no other workload rotates); the fused launches of the
+    # headline share come before the first backward dispatch.  (The steps
+    # grid of every share has one resident workgroup per CU, so grid sizes
+    # do not tell the shares apart.)
+    def windows(rows):
         first = lambda pred: min((int(r["Dispatch_Id"]) for r in rows if pred(r)),
                                  default=1 << 62)
-        bwd = first(lambda r: _short_kernel(r["Kernel_Name"]).startswith("attn_bwd"))
-        w5 = WORKLOADS["bf16_gqa_s128k_cp16_rope"]
-        g5 = steps_grid_lanes(w5, w5.rank)
-        c5 = first(lambda r: _short_kernel(r["Kernel_Name"]) == "attn_steps_bf16"
-                   and int(r[grid_key]) == g5)
-        return bwd, c5
+        name = lambda r: _short_kernel(r["Kernel_Name"])
+        return {"bwd": first(lambda r: name(r).startswith("attn_bwd")),
+                "per_step": first(lambda r: name(r).startswith("attn_step_bf16")),
+                "c5": first(lambda r: name(r).startswith("partition_rope"))}
+
+    def steps_of(rows, w_name, value, last=None):
+        """Values of the steps-grid dispatches of the headline or the 128k share
+        (the last `last` of them: a leg's warm-up and timed launches come after
+        its pre-warm)."""
+        win = windows(rows)
+        lo, hi = (win["c5"], 1 << 62) if w_name == "bf16_gqa_s128k_cp16_rope" else (
+            0, win["per_step"])
+        sel = sorted((r for r in rows if _short_kernel(r["Kernel_Name"]) == "attn_steps_bf16"
+                      and lo <= int(r["Dispatch_Id"]) < hi), key=lambda r: int(r["Dispatch_Id"]))
+        return [value(r) for r in (sel[-last:] if last else sel)]
 
     def fused_of(rows, grid_key, w_name, value):
         """Values of the fused dispatches of one workload's share."""
-        bwd, c5 = windows(rows, grid_key)
+        win = windows(rows)
         g = fused_grid_lanes(WORKLOADS[w_name])
-        lo, hi = (c5, 1 << 62) if w_name == "bf16_gqa_s128k_cp16_rope" else (0, bwd)
+        lo, hi = (win["c5"], 1 << 62) if w_name == "bf16_gqa_s128k_cp16_rope" else (0, win["bwd"])
         if w_name not in (HEADLINE, "bf16_gqa_s128k_cp16_rope"):
             lo, hi = 0, 1 << 62
         return [value(r) for r in rows
@@ -392,15 +395,19 @@ def digest(prof_dir):
     for (k, g), v in sorted(byg.items()):
         lines.append(f"{k:34s} {g:11d} {len(v):6d} {mean(v) / 1e3:10.2f} {min(v) / 1e3:10.2f} "
                      f"{max(v) / 1e3:10.2f}")
-    lines.append("(grids shared by two workloads are split by dispatch order below)")
+    lines.append("(launches of several shares on one kernel and grid are split by dispatch "
+                 "order below)")
     lines.append("")
+    # the headline leg's warm-up and timed launches
+    m = re.search(r"--steps (\d+) --warmup (\d+)", cmd["trace"])
+    timed = int(m.group(1)) + int(m.group(2))
     for name in (HEADLINE, "bf16_gqa_s8k_cp4", "bf16_mha_s16k_cp4_widelogits",
                  "bf16_gqa_s128k_cp16_rope"):
         wc = WORKLOADS[name]
-        g = steps_grid_lanes(wc, wc.rank)
-        v = byg.get(("attn_steps_bf16", g))
+        v = (steps_of(trace, name, dur_of, timed if name == HEADLINE else None)
+             if name in (HEADLINE, "bf16_gqa_s128k_cp16_rope") else [])
         if v:
-            lines.append(f"{name} rank {wc.rank}: attn_steps_bf16 grid {g}: {len(v)} launches, "
+            lines.append(f"{name} rank {wc.rank}: attn_steps_bf16: {len(v)} launches, "
                          f"mean {mean(v) / 1e3:.2f} us, {wc.rank_flops():.4e} FLOP per launch, "
                          f"{wc.rank_flops() / mean(v) * 1e-3:.1f} TFLOP/s")
         fv = fused_of(trace, "Grid_Size_X", name, dur_of)
@@ -408,7 +415,7 @@ def digest(prof_dir):
             lines.append(f"{name} rank {wc.rank}: attn_fused_bf16 grid {fused_grid_lanes(wc)}: "
                          f"{len(fv)} launches, mean {mean(fv) / 1e3:.2f} us, "
                          f"{wc.rank_flops() / mean(fv) * 1e-3:.1f} TFLOP/s")
-    v = byg.get(("attn_steps_bf16", steps_grid_lanes(w, w.rank)))
+    v = steps_of(trace, HEADLINE, dur_of, timed)
     if v:
         lines.append(f"attention_avg_launch_us: {mean(v) / 1e3:.3f}")
         lines.append(f"attention_tflops_from_trace: {w.rank_flops() / mean(v) * 1e-3:.1f}")
@@ -466,9 +473,13 @@ def digest(prof_dir):
         lines.append(f"{k:34s} {g:11d} {len(v):3d} {mean(v):12.0f} {mean(wv):12.0f} "
                      f"{scaled / 1e6:10.1f}")
     lines.append("")
-    a = scaled_of.get(("attn_steps_bf16", steps_grid_lanes(w, w.rank)))
-    if a is not None:
-        lines.append(f"attention_traffic_bytes_per_launch: {a:.0f}")
+    sf = steps_of([r for r in fetch_rows if r["Counter_Name"] == "FETCH_SIZE"], HEADLINE,
+                  lambda r: float(r["Counter_Value"]))
+    sw = steps_of([r for r in write_rows if r["Counter_Name"] == "WRITE_SIZE"], HEADLINE,
+                  lambda r: float(r["Counter_Value"]))
+    if sf and sw:
+        lines.append(f"attention_traffic_bytes_per_launch: "
+                     f"{(mean(sf) * f_fetch + mean(sw) * f_write) * 1024:.0f}")
     ff = fused_of([r for r in fetch_rows if r["Counter_Name"] == "FETCH_SIZE"], "Grid_Size",
                   HEADLINE, lambda r: float(r["Counter_Value"]))
     fw = fused_of([r for r in write_rows if r["Counter_Name"] == "WRITE_SIZE"], "Grid_Size",
@@ -479,13 +490,19 @@ def digest(prof_dir):
     out_files[f"attn_steps_bf16__{w.name}__hbm_traffic.txt"] = lines
 
     # SQ counters: instruction mix and MFMA busy fraction per (kernel, grid)
-    sq, _ = counters("p3")
+    sq, sq_rows = counters("p3")
+    # the steps grids of the headline share get their own entry
+    head = collections.defaultdict(list)
+    for r in steps_of(sq_rows, HEADLINE, lambda r: r):
+        head[("attn_steps_bf16 (headline share)", 0, r["Counter_Name"])].append(
+            float(r["Counter_Value"]))
+    sq.update(head)
     lines = [f"# SQ counters per dispatch (sums over the device), bf16 workloads",
              f"# command: {cmd['p3']}", f"# summary: python3 bench.py --digest {prof_dir}",
              f"# kernel source sha256 ({' + '.join(KERNEL_SOURCES)}): {src}"]
     names = sorted({c for (_, _, c) in sq})
     for k, g in sorted({(k, g) for (k, g, _) in sq}):
-        lines.append(f"{k} grid={g}")
+        lines.append(f"{k} grid={g}" if g else k)
         for c in names:
             v = sq.get((k, g, c))
             if v:

@@ -70,6 +70,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 namespace cpattn {
 namespace {
 
@@ -661,18 +663,14 @@ struct StepsParams {
     const uint16_t *q;
     int64_t two_c;
     int hq, hkv, group, nruns, items;   // items: workgroups per (batch, KV head)
+    int total;                          // items of the grid; > gridDim.x: workgroups loop
     float scale_log2;
     StepDesc st[MAX_STEPS];
     WorkRun run[MAX_RUNS];
 };
 static_assert(sizeof(StepsParams) <= 4096, "kernel arguments");
 
-__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_steps_bf16(StepsParams sp) {
-    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
-    // workgroup -> (batch, KV head), then the run, then (query tile, head in
-    // group) inside it; the runs are laid out longest first across all steps
-    const int item = xcd_order(blockIdx.x, gridDim.x);
+__device__ __forceinline__ void steps_item(const StepsParams &sp, int item, char *lds) {
     const int ng = item / sp.items;
     int w = item - ng * sp.items;
     int j = 0;
@@ -701,6 +699,31 @@ attn_steps_bf16(StepsParams sp) {
         Kernel<StepPlan<true>, false>::run_item(p, lds, n, g, hh, qt);
     else
         Kernel<StepPlan<false>, false>::run_item(p, lds, n, g, hh, qt);
+}
+
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_steps_bf16(StepsParams sp) {
+    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
+    // workgroup -> (batch, KV head), then the run, then (query tile, head in
+    // group) inside it; the runs are laid out longest first across all steps
+    if (sp.total == (int)gridDim.x) {
+        steps_item(sp, xcd_order(blockIdx.x, gridDim.x), lds);
+        return;
+    }
+    // Fewer workgroups than items (one per CU, a multiple of 8 of each):
+    // workgroup b serves the items of XCD b % 8's contiguous range (longest
+    // first) round by round, in alternating directions, so each CU's items
+    // add up to about the same work.  A workgroup that stays resident skips
+    // the launch of a new one and its last item's stores drain while the
+    // next item starts.
+    const int xq = blockIdx.x & 7, slot = blockIdx.x >> 3, nslot = gridDim.x >> 3;
+    const int range = sp.total >> 3;
+    for (int r = 0; r * nslot < range; ++r) {
+        const int li = r * nslot + ((r & 1) ? nslot - 1 - slot : slot);
+        if (li >= range) continue;
+        if (r > 0) lds_barrier();   // every wave is done with the LDS of the last item
+        steps_item(sp, xq * range + li, lds);
+    }
 }
 
 // A rank's whole share (merged output, fp32 or bf16).
@@ -739,6 +762,21 @@ hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, con
     p.scale_log2 = g.scale_log2;
     if (g.causal) return launch_kernel(attn_step_bf16<true>, p, g.b, g.hq, stream);
     return launch_kernel(attn_step_bf16<false>, p, g.b, g.hq, stream);
+}
+
+// Workgroups of the steps grid that fit at once (one per CU: the LDS ring
+// takes 128 KiB), a multiple of 8; 0 if the device cannot be queried.
+static int resident_slots() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n & ~7;
 }
 
 hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void *const *k,
@@ -803,7 +841,12 @@ hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void
     }
     sp.nruns = nr;
     sp.items = items;
-    const int64_t blocks = (int64_t)items * sp.hkv * g[0].b;
+    const int64_t total = (int64_t)items * sp.hkv * g[0].b;
+    sp.total = (int)total;
+    // one resident workgroup per CU when there are more than two items per
+    // CU and the items split evenly over the 8 XCD ranges
+    const int64_t slots = resident_slots();
+    const int64_t blocks = (slots >= 8 && total % 8 == 0 && total > 2 * slots) ? slots : total;
     hipLaunchKernelGGL(attn_steps_bf16, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, sp);
     return hipGetLastError();
 }

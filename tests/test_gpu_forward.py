@@ -130,7 +130,10 @@ def test_forward_fp32_full_size():
 def test_stepwise_calls_equal_forward_entry_point(name, s):
     """One launch per step (cpattn_step_fwd), all steps in one grid
     (cpattn_forward_steps) and cpattn_forward give the same bits: every
-    partial of every rank, and the merged result."""
+    partial of every rank, and the merged result.  At s = 2*8*300 the grid
+    has 1088-1536 query tiles, more than two per CU, so its workgroups loop
+    over their items (ranks 0-2 and 4-6 with a partial last round); the
+    per-step launches take one item per workgroup."""
     w = EXTRA[name] if name in EXTRA else small(WORKLOADS[name], s)
     say(f"stepwise vs cpattn_forward_steps vs cpattn_forward: {name} s={s}")
     q, k, v = make_inputs(w)

@@ -44,7 +44,6 @@
 
 #include <math.h>
 
-#include <vector>
 
 namespace cpattn {
 namespace {
@@ -869,34 +868,46 @@ attn_bwd_dkdv(BwdParams p) {
 // which no other step of the share touches, so a workgroup takes all query
 // heads of its KV group (no head split, no atomics) and the steps'
 // workgroups share the machine instead of running in rounds of equal
-// workgroups.  The host orders the steps longest workgroups first.  The
-// key tiles of packed samples are numbered sample by sample: p.tab.tile0
-// for the modes that see 2c keys of a sample, tile0_half for
-// kv_first_half (c keys).
+// workgroups.  The key tiles of packed samples are numbered sample by
+// sample: p.tab.tile0 for the modes that see 2c keys of a sample,
+// tile0_half for kv_first_half (c keys).  Workgroups come in runs of key
+// tiles of one step that see about the same query rows (a non-causal step
+// is one run; each key tile of the causal step, which sees rows from its
+// first key on, is a run of its own), laid out by the host longest first.
 constexpr int MAX_BWD_STEPS = 32;
+constexpr int MAX_KV_RUNS = 64;
 struct KvStepDesc {
     const uint16_t *k, *v;
     float *dk, *dv;
-    int mode, item0;          // first workgroup of the step in the grid
+    int mode;
+};
+struct KvRun {
+    int step, kt0;            // the step (index into st) and its first key tile
+    int item0;                // first workgroup of the run in the grid
 };
 struct DkdvStepsParams {
     BwdParams p;              // the rank's Q side, dims, scale, sample table
     int32_t tile0_half[CPATTN_MAX_SEQS + 1];
-    int nsteps;
+    int nruns;
     KvStepDesc st[MAX_BWD_STEPS];
+    KvRun run[MAX_KV_RUNS];
 };
+static_assert(sizeof(DkdvStepsParams) <= 4096, "kernel arguments");
 
 __global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_steps(DkdvStepsParams sp) {
     __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
     const int item = blockIdx.x;
     int j = 0;
-    while (j + 1 < sp.nsteps && sp.st[j + 1].item0 <= item) ++j;
-    const KvStepDesc &d = sp.st[j];
+    while (j + 1 < sp.nruns && sp.run[j + 1].item0 <= item) ++j;
+    const KvRun &rn = sp.run[j];
+    const KvStepDesc &d = sp.st[rn.step];
+    const int inner = sp.p.hkv * sp.p.b;   // workgroups per key tile
+    const int w = item - rn.item0;
     dkdv_item<true>(sp.p,
-              KvStep{d.k, d.v, d.dk, d.dv, d.mode, 1,
-                     d.mode == CPATTN_KV_FIRST_HALF ? sp.tile0_half : sp.p.tab.tile0},
-              item - d.item0, lds);
+                    KvStep{d.k, d.v, d.dk, d.dv, d.mode, 1,
+                           d.mode == CPATTN_KV_FIRST_HALF ? sp.tile0_half : sp.p.tab.tile0},
+                    (rn.kt0 + w / inner) * inner + w % inner, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1056,17 +1067,6 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &
                                       const void *const *v, const void *dout,
                                       const float *lse, const float *delta, float *const *dk,
                                       float *const *dv, hipStream_t stream) {
-    // longest workgroups first: kv_first_half key tiles (every query row),
-    // q_second_half tiles (the second chunk's rows), then the causal step
-    // (its first key tiles see the most rows)
-    std::vector<int> order(n);
-    int m = 0;
-    for (int pass = 0; pass < 3; ++pass)
-        for (int i = 0; i < n; ++i) {
-            const int cls = mode[i] == CPATTN_KV_FIRST_HALF ? 0
-                            : mode[i] == CPATTN_Q_SECOND_HALF ? 1 : 2;
-            if (cls == pass) order[m++] = i;
-        }
     for (int j0 = 0; j0 < n; j0 += MAX_BWD_STEPS) {
         const int nb = n - j0 < MAX_BWD_STEPS ? n - j0 : MAX_BWD_STEPS;
         DkdvStepsParams sp = {};
@@ -1076,19 +1076,51 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &
         BwdParams half = sp.p;
         const int64_t kt_half = fill_tiles(half, tab, CPATTN_KV_FIRST_HALF, true);
         for (int i = 0; i <= tab.nseq; ++i) sp.tile0_half[i] = half.tab.tile0[i];
-        sp.nsteps = nb;
-        int64_t items = 0;
+        // runs: (step, first key tile, key tiles, query rows each key tile sees)
+        int rs[MAX_KV_RUNS], rk[MAX_KV_RUNS], rc[MAX_KV_RUNS];
+        int64_t rl[MAX_KV_RUNS];
+        int nr = 0, ncausal = 0;
+        for (int jj = 0; jj < nb; ++jj) ncausal += mode[j0 + jj] == CPATTN_CAUSAL ? 1 : 0;
+        const int64_t two_c = g[0].two_c;
         for (int jj = 0; jj < nb; ++jj) {
-            const int i = order[j0 + jj];
-            KvStepDesc &d = sp.st[jj];
-            d.k = (const uint16_t *)k[i];
-            d.v = (const uint16_t *)v[i];
-            d.dk = dk[i];
-            d.dv = dv[i];
-            d.mode = mode[i];
-            d.item0 = (int)items;
-            items += (mode[i] == CPATTN_KV_FIRST_HALF ? kt_half : kt_full) * g[0].hkv * g[0].b;
+            const int i = j0 + jj;
+            sp.st[jj] = KvStepDesc{(const uint16_t *)k[i], (const uint16_t *)v[i], dk[i], dv[i],
+                                   mode[i]};
+            const int nkt = (int)(mode[i] == CPATTN_KV_FIRST_HALF ? kt_half : kt_full);
+            if (mode[i] != CPATTN_CAUSAL || tab.nseq > 1) {
+                // every key tile sees the same rows (kv_first_half: all 2c,
+                // q_second_half: the second c; packed samples: one run)
+                rs[nr] = jj;
+                rk[nr] = 0;
+                rc[nr] = nkt;
+                rl[nr++] = mode[i] == CPATTN_Q_SECOND_HALF ? two_c / 2 : two_c;
+                continue;
+            }
+            // causal: key tile kt sees the rows from its first key on
+            const int room = (MAX_KV_RUNS - (nb - ncausal)) / ncausal;
+            const int per = (nkt + room - 1) / room;   // key tiles per run
+            for (int kt = 0; kt < nkt; kt += per) {
+                rs[nr] = jj;
+                rk[nr] = kt;
+                rc[nr] = nkt - kt < per ? nkt - kt : per;
+                rl[nr++] = two_c - (int64_t)kt * TR * KW;
+            }
         }
+        // longest first (stable: ties keep step order)
+        for (int a = 1; a < nr; ++a)
+            for (int b2 = a; b2 > 0 && rl[b2 - 1] < rl[b2]; --b2) {
+                int t = rs[b2]; rs[b2] = rs[b2 - 1]; rs[b2 - 1] = t;
+                t = rk[b2]; rk[b2] = rk[b2 - 1]; rk[b2 - 1] = t;
+                t = rc[b2]; rc[b2] = rc[b2 - 1]; rc[b2 - 1] = t;
+                const int64_t tl = rl[b2]; rl[b2] = rl[b2 - 1]; rl[b2 - 1] = tl;
+            }
+        const int64_t inner = (int64_t)g[0].hkv * g[0].b;
+        int64_t items = 0;
+        for (int a = 0; a < nr; ++a) {
+            sp.run[a] = KvRun{rs[a], rk[a], (int)items};
+            items += rc[a] * inner;
+        }
+        sp.nruns = nr;
         hipLaunchKernelGGL(attn_bwd_dkdv_steps, dim3((unsigned)items), dim3(64 * NWK), 0,
                            stream, sp);
         const hipError_t e = hipGetLastError();

@@ -1082,11 +1082,27 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &
         int nr = 0, ncausal = 0;
         for (int jj = 0; jj < nb; ++jj) ncausal += mode[j0 + jj] == CPATTN_CAUSAL ? 1 : 0;
         const int64_t two_c = g[0].two_c;
+        // packed samples: a run per (step, sample) when the table holds them
+        const bool per_sample = tab.nseq > 1 && nb * tab.nseq <= MAX_KV_RUNS;
         for (int jj = 0; jj < nb; ++jj) {
             const int i = j0 + jj;
             sp.st[jj] = KvStepDesc{(const uint16_t *)k[i], (const uint16_t *)v[i], dk[i], dv[i],
                                    mode[i]};
             const int nkt = (int)(mode[i] == CPATTN_KV_FIRST_HALF ? kt_half : kt_full);
+            if (per_sample) {
+                // the sample's key tiles (causal: first tile first) see at
+                // most its 2c rows (q_second_half: its second c)
+                const int32_t *t0 =
+                    mode[i] == CPATTN_KV_FIRST_HALF ? sp.tile0_half : sp.p.tab.tile0;
+                for (int q = 0; q < tab.nseq; ++q) {
+                    const int64_t two_cq = tab.lcu[q + 1] - tab.lcu[q];
+                    rs[nr] = jj;
+                    rk[nr] = t0[q];
+                    rc[nr] = t0[q + 1] - t0[q];
+                    rl[nr++] = mode[i] == CPATTN_Q_SECOND_HALF ? two_cq / 2 : two_cq;
+                }
+                continue;
+            }
             if (mode[i] != CPATTN_CAUSAL || tab.nseq > 1) {
                 // every key tile sees the same rows (kv_first_half: all 2c,
                 // q_second_half: the second c; packed samples: one run)

@@ -188,10 +188,13 @@ __device__ __forceinline__ void copy_rows(const uint16_t *base, int64_t row_byte
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup = 4 waves x 32 query rows of one (batch, head); 32-key tiles
-// of K and V stream through NSQ stages, PDQ tiles ahead.  Each wave copies
-// rows 4w.. and 4(w+4).. of both tiles.
-constexpr int NWB = 4;
+// dQ: workgroup = NW waves (4 or 8) x 32 query rows of one (batch, head);
+// 32-key tiles of K and V stream through NSQ stages, PDQ tiles ahead.  Wave
+// w copies rows 4w.. (and, with 4 waves, 4(w+4)..) of both tiles.  With 8
+// waves a copied tile serves twice the rows (one workgroup per CU instead of
+// two); the share's launcher takes 8 when that still leaves two workgroups
+// per CU.
+constexpr int NWB = 4;                     // waves of the single step's dq
 constexpr int NSQ = 4;
 constexpr int PDQ = NSQ - 1;
 constexpr int STAGE_DQ = 2 * TB;           // K, V
@@ -215,7 +218,8 @@ struct DqStepPlan {
     int qrow0, nq, nk, ntiles;
     bool causal;
     static constexpr int c = 0;   // no block is seen by the second chunk only
-    __device__ __forceinline__ void init(const BwdParams &p, int smp, int q0, int n, int g) {
+    __device__ __forceinline__ void init(const BwdParams &p, int smp, int q0, int n, int g,
+                                         int tile_rows) {
         const Geo G = geo_of(p, smp, p.mode);
         qrow0 = G.qrow0;
         nq = G.nq;
@@ -223,7 +227,7 @@ struct DqStepPlan {
         causal = G.causal;
         kb = p.k + (((int64_t)n * p.two_c + G.kv0) * p.hkv + g) * D;
         vb = p.v + (((int64_t)n * p.two_c + G.kv0) * p.hkv + g) * D;
-        const int kend = causal ? min(nk, q0 + TR * NWB) : nk;
+        const int kend = causal ? min(nk, q0 + tile_rows) : nk;
         ntiles = (kend + TR - 1) / TR;
     }
     __device__ __forceinline__ DqCursor first() const {
@@ -244,7 +248,8 @@ struct DqSharePlan {
     int64_t block;
     int r, cp, c, nAB, kend, ntiles;
     int qrow0, nq;
-    __device__ __forceinline__ void init(const BwdParams &p, int smp, int q0, int n, int g) {
+    __device__ __forceinline__ void init(const BwdParams &p, int smp, int q0, int n, int g,
+                                         int tile_rows) {
         const int l0 = p.tab.lcu[smp];
         c = (p.tab.lcu[smp + 1] - l0) >> 1;
         qrow0 = l0;
@@ -255,8 +260,8 @@ struct DqSharePlan {
         r = p.rank;
         cp = p.cp;
         const int cA = (c + TR - 1) / TR, cB = (2 * c + TR - 1) / TR;
-        nAB = (q0 + TR * NWB > c) ? cp - 1 - r : 0;
-        kend = min(2 * c, q0 + TR * NWB);
+        nAB = (q0 + tile_rows > c) ? cp - 1 - r : 0;
+        kend = min(2 * c, q0 + tile_rows);
         ntiles = r * cA + nAB * cB + (kend + TR - 1) / TR;
     }
     __device__ __forceinline__ DqCursor block_of(int see) const {
@@ -291,8 +296,9 @@ struct DqSharePlan {
 
 // PREP: p.lse and p.delta hold -L/scale and -D (launch_bwd_prep) instead
 // of L and D.
-template <class Plan, bool ACCUMULATE, bool PREP>
+template <class Plan, bool ACCUMULATE, bool PREP, int NW>
 __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
+    constexpr int CPW = 8 / NW;   // 4-row copies per wave and tensor per tile
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
@@ -314,10 +320,10 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
     const int head = g * p.group + hh;
     const int smp = seq_of(p.tab.tile0, p.tab.nseq, qt_all);
     const int qt = qt_all - p.tab.tile0[smp];
-    const int q0 = qt * TR * NWB;
+    const int q0 = qt * TR * NW;
     const int wrow0 = q0 + wave * TR;
     Plan P;
-    P.init(p, smp, q0, n, g);
+    P.init(p, smp, q0, n, g, TR * NW);
     const int ntiles = P.ntiles;
 
     LaneOffsets L;
@@ -345,26 +351,26 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
         for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
 
     const int64_t row_bytes = (int64_t)p.hkv * D * 2;
-    const unsigned coff = copy_offset(lane, wave, row_bytes);   // m = wave, wave + 4
+    const unsigned coff = copy_offset(lane, wave, row_bytes);   // m = wave (+ NW)
     // copy cursor (tile cu); tiles past the last repeat it, so every wave
-    // issues 4 copies per tile
+    // issues 2 CPW copies per tile
     DqCursor CC = P.first();
     int cu = 0;
     auto issue = [&](int stage) {
         const unsigned sb = lbase + stage * STAGE_DQ;
         if (CC.key0 + TR <= CC.nk) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int m = wave + 4 * i;
+            for (int i = 0; i < CPW; ++i) {
+                const int m = wave + NW * i;
                 dma16((const char *)CC.kb + (CC.key0 + 4 * m) * row_bytes, coff, sb + m * 1024);
                 dma16((const char *)CC.vb + (CC.key0 + 4 * m) * row_bytes, coff,
                       sb + TB + m * 1024);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                copy_rows(CC.kb, row_bytes, CC.key0, CC.nk, wave + 4 * i, coff, sb, lane);
-                copy_rows(CC.vb, row_bytes, CC.key0, CC.nk, wave + 4 * i, coff, sb + TB, lane);
+            for (int i = 0; i < CPW; ++i) {
+                copy_rows(CC.kb, row_bytes, CC.key0, CC.nk, wave + NW * i, coff, sb, lane);
+                copy_rows(CC.vb, row_bytes, CC.key0, CC.nk, wave + NW * i, coff, sb + TB, lane);
             }
         }
     };
@@ -380,7 +386,7 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
             issue(i);
             advance();
         }
-        wait_vmcnt<4 * (PDQ - 1)>();
+        wait_vmcnt<2 * CPW * (PDQ - 1)>();
     }
     lds_barrier();
     // the lane's LDS read offsets in a tile (the stage base is added per read)
@@ -468,7 +474,7 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
                 for (int dt = 0; dt < D / 32; ++dt)
                     acc[dt] = MFMA(at[kc][dt], dsb[kc], acc[dt], 0, 0, 0);
         }
-        wait_vmcnt<4 * (PDQ - 1)>();   // tile t + 1 has landed
+        wait_vmcnt<2 * CPW * (PDQ - 1)>();   // tile t + 1 has landed
         lds_barrier();
         stage = stage + 1 == NSQ ? 0 : stage + 1;
         if (t + 1 < ntiles) P.next(T);
@@ -495,15 +501,16 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
 __global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
-    dq_body<DqStepPlan, true, false>(p, lds);
+    dq_body<DqStepPlan, true, false, NWB>(p, lds);
 }
 
 // The dq of all cp steps of a rank's share in one grid: a workgroup streams
 // every step's keys for its query tile and writes dq once.
-__global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_share(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
-    dq_body<DqSharePlan, false, true>(p, lds);
+    dq_body<DqSharePlan, false, true, NW>(p, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1009,10 +1016,10 @@ BwdParams make_params(const StepGeom &g, const SeqTable &tab, int mode, const vo
     return p;
 }
 
-// each sample's query rows (dq: tiles of TR * NWB rows) or keys (dK/dV:
+// each sample's query rows (dq: tiles of TR * nw rows) or keys (dK/dV:
 // tiles of TR * KW keys) in this mode, into p.tab.tile0; returns the total
-int64_t fill_tiles(BwdParams &p, const SeqTable &tab, int mode, bool keys) {
-    const int per_tile = keys ? TR * KW : TR * NWB;
+int64_t fill_tiles(BwdParams &p, const SeqTable &tab, int mode, bool keys, int nw = NWB) {
+    const int per_tile = keys ? TR * KW : TR * nw;
     p.tab.tile0[0] = 0;
     for (int i = 0; i < tab.nseq; ++i) {
         const int c = (tab.lcu[i + 1] - tab.lcu[i]) / 2;
@@ -1055,9 +1062,18 @@ hipError_t launch_bwd_dq_share_bf16(const StepGeom &g, const SeqTable &tab, int 
     p.rank = rank;
     p.cp = cp;
     p.block_elems = g.b * g.two_c * g.hkv * D;
-    // query tiles of the 2c local rows of every sample
-    const int64_t nqt = fill_tiles(p, tab, CPATTN_CAUSAL, false);
-    hipLaunchKernelGGL(attn_bwd_dq_share, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * NWB), 0,
+    // query tiles of the 2c local rows of every sample: 256-row tiles (8
+    // waves) when they still give two workgroups per CU and no sample is
+    // packed (short samples would leave half of a tile's waves idle), else
+    // 128-row ones
+    const int64_t nqt8 = fill_tiles(p, tab, CPATTN_CAUSAL, false, 8);
+    if (tab.nseq == 1 && nqt8 * g.hq * g.b >= 2 * (int64_t)device_cu_count()) {
+        hipLaunchKernelGGL(attn_bwd_dq_share<8>, dim3((unsigned)(nqt8 * g.hq * g.b)), dim3(64 * 8),
+                           0, stream, p);
+        return hipGetLastError();
+    }
+    const int64_t nqt = fill_tiles(p, tab, CPATTN_CAUSAL, false, 4);
+    hipLaunchKernelGGL(attn_bwd_dq_share<4>, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * 4), 0,
                        stream, p);
     return hipGetLastError();
 }

@@ -764,9 +764,7 @@ hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, con
     return launch_kernel(attn_step_bf16<false>, p, g.b, g.hq, stream);
 }
 
-// Workgroups of the steps grid that fit at once (one per CU: the LDS ring
-// takes 128 KiB), a multiple of 8; 0 if the device cannot be queried.
-static int resident_slots() {
+int device_cu_count() {
     static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -776,8 +774,12 @@ static int resident_slots() {
             return 0;
         cus[dev].store(n, std::memory_order_relaxed);
     }
-    return n & ~7;
+    return n;
 }
+
+// Workgroups of the steps grid that fit at once (one per CU: the LDS ring
+// takes 128 KiB), a multiple of 8.
+static int resident_slots() { return device_cu_count() & ~7; }
 
 hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void *const *k,
                              const void *const *v, float *const *o, float *const *lse,

@@ -118,6 +118,10 @@ hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, const float *o, con
                            const float *lse, float inv_scale, float *nl, float *nd,
                            hipStream_t stream);
 
+// Compute units of the current device (cached per device), 0 if it cannot
+// be queried.
+int device_cu_count();
+
 // x[0 .. n) = 0 (n a multiple of 4, x 16-byte aligned).
 hipError_t launch_fill_zero(float *x, int64_t n, hipStream_t stream);
 

@@ -158,3 +158,37 @@ def test_backward_full_size_sampled_dq():
     say(f"  oracle on {len(rows)} rows")
     dq_ref, _, _ = attention_rows_bwd(qf, kf, vf, dof, pos + 1)
     assert_grad("dQ rows", g["dq"].cpu().numpy()[:, rows], dq_ref)
+
+
+@pytest.mark.parametrize("name", ["bf16_gqa_s32k_cp8", "bf16_mha_s16k_cp4_widelogits"])
+def test_backward_full_size_equals_step_entry_points(name):
+    """At full size every element of the share's gradients (the one-grid dK/dV
+    and the dQ grid of 256-row tiles that these sizes select) against the
+    same share through cpattn_step_bwd, one zigzag step at a time; that entry
+    point is held to the oracle per mode above.  The two differ only in the
+    order of the fp32 sums, so the bound is the same relative one."""
+    w = WORKLOADS[name]
+    r = w.rank
+    say(f"backward full {name}: rank {r}, share vs per-step entry points")
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    del q, k, v
+    doz_r = to_device(f32_to_bf16_bits(ocp.partition(as_f32(_dout(w)), w.cp)[r]
+                                       .astype(np.float32)))
+    buf = P.alloc_rank(r, C.CPATTN_F32)
+    P.forward(buf)
+    g = P.alloc_grads(r)
+    P.backward(g, buf["o"], buf["lse"], doz_r)
+    # the per-step path takes D = rowsum(dO * O) as [b, hq, 2c]
+    delta = (doz_r.float() * buf["o"]).sum(-1).transpose(1, 2).contiguous()
+    dq = torch.zeros_like(g["dq"])
+    dkz, dvz = torch.zeros_like(g["dkz"]), torch.zeros_like(g["dvz"])
+    for i in range(w.cp):
+        mode, src = C.cpattn_step_mode(i, r, w.cp)
+        C.cpattn_step_bwd(P.dims, C.CPATTN_BF16, 0.0, mode, P.qz[r], P.kz[src], P.vz[src],
+                          doz_r, buf["lse"], delta, dq, dkz[src], dvz[src])
+    torch.cuda.synchronize()
+    assert_grad("dQ", g["dq"].cpu().numpy(), dq.cpu().numpy())
+    assert_grad("dK", g["dkz"].cpu().numpy(), dkz.cpu().numpy())
+    assert_grad("dV", g["dvz"].cpu().numpy(), dvz.cpu().numpy())

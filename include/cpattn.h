@@ -55,7 +55,7 @@ typedef struct cpattn_dims {
     int64_t s;    /* full sequence length, a multiple of 2*cp                 */
     int32_t hq;   /* query heads, a multiple of hkv                           */
     int32_t hkv;  /* key/value heads (GQA groups)                              */
-    int32_t d;    /* head dimension: 128 (every path); 64 (the fp32 path only) */
+    int32_t d;    /* head dimension: 64 or 128 (the bf16 backward: 128 only) */
     int32_t cp;   /* context-parallel size (ranks emulated), >= 1: any cp with
                      s % (2*cp) == 0, down to chunks of one row (c = 1)       */
 } cpattn_dims;
@@ -154,8 +154,8 @@ int cpattn_partition(const cpattn_dims *dims, int dtype, int h, const void *x,
 /* One step's blockwise attention ("Megatron-LM 篇" 3.2 step 2 and 3.4),
  * device.  q_r: rank's partitioned Q block [b, 2c, hq, d]; k_src, v_src:
  * the source rank's partitioned K and V blocks [b, 2c, hkv, d].  All three
- * have element type 'dtype' (CPATTN_BF16: bf16 MFMA with fp32 accumulation,
- * d = 128; CPATTN_F32: fp32 throughout, the debug path, d = 64 or 128).  mode: CPATTN_CAUSAL,
+ * have element type 'dtype' (CPATTN_BF16: bf16 MFMA with fp32 accumulation;
+ * CPATTN_F32: fp32 throughout, the debug path), d = 64 or 128.  mode: CPATTN_CAUSAL,
  * CPATTN_KV_FIRST_HALF or CPATTN_Q_SECOND_HALF.
  * Writes o [b, rows, hq, d] fp32 (normalised within the step) and
  * lse [b, hq, rows] fp32, rows = 2c (first two modes) or c (the last one,
@@ -250,7 +250,7 @@ int cpattn_forward_noalloc(const cpattn_dims *dims, int dtype, float scale, int 
  * correction happens in place: no partials, no merge, no workspace.  The
  * result is the one cpattn_forward gives, up to rounding order.
  * qz, kz, vz: partitioned [cp, b, 2c, h, d] bf16 (CPATTN_BF16 only,
- * EDTYPE otherwise; d = 128, ESHAPE otherwise).  o_out [b, 2c, hq, d] in
+ * EDTYPE otherwise; d = 64 or 128, ESHAPE otherwise).  o_out [b, 2c, hq, d] in
  * out_dtype (CPATTN_F32, or CPATTN_BF16 rounded to nearest even); lse_out
  * [b, hq, 2c] fp32 natural log, or NULL.  Pointers 16-byte aligned (lse_out
  * 4-byte), EALIGN otherwise.  Asynchronous on 'stream'. */
@@ -325,8 +325,8 @@ int cpattn_partition_varlen(const cpattn_dims *dims, int dtype, int h, const cpa
 /* cpattn_forward_fused_varlen, device: rank 'rank''s whole forward share of
  * a packed batch in one launch.  Each sample's rows stream the key blocks
  * of the cp ring steps of that sample only (cpattn_forward_fused on every
- * sample at once).  qz, kz, vz [cp, b, s/cp, h, 128] bf16 as written by
- * cpattn_partition_varlen; o_out [b, s/cp, hq, 128] (out_dtype); lse_out
+ * sample at once).  qz, kz, vz [cp, b, s/cp, h, d] bf16 as written by
+ * cpattn_partition_varlen; o_out [b, s/cp, hq, d] (out_dtype); lse_out
  * [b, hq, s/cp] or NULL.  Types, alignment and errors as
  * cpattn_forward_fused. */
 int cpattn_forward_fused_varlen(const cpattn_dims *dims, int dtype, float scale, int rank,

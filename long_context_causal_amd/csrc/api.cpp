@@ -243,7 +243,6 @@ int cpattn_step_fwd(const cpattn_dims *dims, int dtype, float scale, int mode,
     if (mode != CPATTN_CAUSAL && mode != CPATTN_KV_FIRST_HALF && mode != CPATTN_Q_SECOND_HALF)
         return CPATTN_EINVAL;
     if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return CPATTN_EDTYPE;
-    if (dtype == CPATTN_BF16 && dims->d != 128) return CPATTN_ESHAPE;
     if (!q_r || !k_src || !v_src || !o || !lse) return CPATTN_EINVAL;
     if (!aligned16(q_r) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(o) ||
         ((uintptr_t)lse & 3u))
@@ -320,7 +319,6 @@ int cpattn_forward_steps(const cpattn_dims *dims, int dtype, float scale, int ra
     if (!qz || !kz || !vz || !ws) return CPATTN_EINVAL;
     if (((uintptr_t)ws & 255u) != 0) return CPATTN_EALIGN;
     if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return CPATTN_EDTYPE;
-    if (dtype == CPATTN_BF16 && dims->d != 128) return CPATTN_ESHAPE;
     if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz)) return CPATTN_EALIGN;
     if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
     if (ws_bytes < cpattn_forward_workspace(dims, rank)) return CPATTN_ENOSPACE;
@@ -419,7 +417,6 @@ int cpattn_forward_fused_varlen(const cpattn_dims *dims, int dtype, float scale,
     if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
     if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
     if (out_dtype != CPATTN_F32 && out_dtype != CPATTN_BF16) return CPATTN_EDTYPE;
-    if (dims->d != 128) return CPATTN_ESHAPE;
     if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz) || !aligned16(o_out) ||
         (lse_out && ((uintptr_t)lse_out & 3u)))
         return CPATTN_EALIGN;
@@ -429,6 +426,7 @@ int cpattn_forward_fused_varlen(const cpattn_dims *dims, int dtype, float scale,
     f.two_c = g.two_c;
     f.hq = dims->hq;
     f.hkv = dims->hkv;
+    f.d = dims->d;
     f.rank = rank;
     f.cp = dims->cp;
     f.scale_log2 = g.scale_log2;

@@ -54,9 +54,11 @@
 //   The result is the same softmax.  p is rounded to bf16 (nearest even) for
 //   the P V product; the row sum l accumulates the fp32 p.
 //
-// LDS (64 banks x 4 bytes on gfx950): rows are 256 bytes; 16-byte chunks
-// are XOR-swizzled per row (K: by the matrix row feeding it, V: by key%4)
-// so every ds_read_b128 / ds_read_b64_tr_b16 phase hits distinct banks.
+// LDS (64 banks x 4 bytes on gfx950): rows are 2d bytes (256 for d = 128,
+// 128 for d = 64, one template per head dimension); 16-byte chunks are
+// XOR-swizzled per row (see Kernel::k_swz / v_swz) so every ds_read_b128 /
+// ds_read_b64_tr_b16 phase hits distinct banks.  With d = 64 a phase of
+// matrix steps does four MFMAs on each of four k-steps instead of eight.
 // The global -> LDS copies are issued from inline assembly, so the compiler
 // does not track them (it would otherwise wait for every copy in flight
 // before each LDS read, as it cannot tell the stages apart); explicit vmcnt
@@ -77,16 +79,13 @@ namespace {
 
 using namespace tiles;
 
-constexpr int D = 128;
 constexpr int BN = 64;                 // keys per LDS tile
 constexpr int NW = 8;                  // waves per workgroup
 constexpr int BM = 32 * NW;            // query rows per workgroup
 constexpr int NS = 4;                  // LDS stages
-constexpr int ROWB = D * 2;            // bytes per K/V row in LDS
-constexpr int TILEB = BN * ROWB;       // bytes per K (or V) tile
-constexpr int KI = BN / 4 / NW;        // copy instructions per wave per tile (each)
-constexpr int LPT = 2 * KI;            // copies per wave per tile (K and V)
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units a stale max may lag
+// bytes of one K (or V) tile in LDS for head dimension D (bf16 rows of D)
+constexpr int tile_bytes(int D) { return BN * D * 2; }
 
 struct Params {
     const uint16_t *q, *k, *v;
@@ -118,9 +117,10 @@ struct TileRef {
 // sequence), qrow0 and nq (the local row of the sequence's query row 0 and
 // its query rows), orow0 and orows (the output row of query row 0 and the
 // output rows per batch element).
-template <bool CAUSAL>
+template <bool CAUSAL, int D>
 struct StepPlan {
     static constexpr bool kLongestFirst = CAUSAL;   // later causal tiles see more keys
+    static constexpr int kD = D;
     const uint16_t *kb, *vb;
     int nk, ntiles;
     int qtile, qrow0, nq, orow0, orows;
@@ -172,8 +172,10 @@ __device__ __forceinline__ int div_by(int u, unsigned m, int d) {
     return q;
 }
 
+template <int D>
 struct FusedPlan {
     static constexpr bool kLongestFirst = true;     // later tiles: second chunk, causal
+    static constexpr int kD = D;
     const uint16_t *k0, *v0;      // rank 0's block, this batch and KV head
     int64_t block;                // elements between consecutive ranks' blocks
     int r, cp, c, cA, nAB, cB, ta, tb, kend, ntiles, q0;
@@ -257,6 +259,26 @@ __device__ __forceinline__ int xcd_order(int blk, int nblk) {
 
 template <class Plan, bool OUT_BF16>
 struct Kernel {
+    static constexpr int D = Plan::kD;
+    static constexpr int ROWB = D * 2;            // bytes per K/V row in LDS
+    static constexpr int TILEB = tile_bytes(D);   // bytes per K (or V) tile
+    static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+    static constexpr int RPC = 64 / CPR;          // tile rows per copy (64 lanes x 16 bytes)
+    static constexpr int KI = BN / RPC / NW;      // copy instructions per wave per tile (each)
+    static constexpr int LPT = 2 * KI;            // copies per wave per tile (K and V)
+    static constexpr int NSTEP = D / 16;          // matrix steps per phase (four MFMAs each)
+    static_assert(D == 64 || D == 128, "head dimension");
+    static_assert(KI >= 1 && BN % (RPC * NW) == 0, "copy split");
+    // LDS chunk c of tile row r holds chunk c ^ k_swz(r) of the K row and
+    // chunk c ^ v_swz(r) of the V row.  256-byte rows (D = 128): K by the
+    // matrix row that reads it, V by r % 4.  128-byte rows (D = 64; two rows
+    // share one pass over the 64 banks): K by r / 2, V by (r / 2) % 2.
+    __device__ __forceinline__ static int k_swz(int r) {
+        return D == 128 ? swap_bits23(r) & 15 : (r >> 1) & 7;
+    }
+    __device__ __forceinline__ static int v_swz(int r) {
+        return D == 128 ? (r & 3) << 2 : ((r >> 1) & 1) << 2;
+    }
     // Per-wave state.
     struct State {
         bf16x8 qf[D / 16];       // Q as the B operand of S^T
@@ -283,7 +305,7 @@ struct Kernel {
             const uint16_t *vb = tr.vb + (int64_t)tr.key0 * S.kstride;
 #pragma unroll
             for (int i = 0; i < KI; ++i) {
-                const unsigned dst = sK + (wave * KI + i) * 4 * ROWB;
+                const unsigned dst = sK + (wave * KI + i) * RPC * ROWB;
                 dma16(kb, S.gk[i], dst);
                 dma16(vb, S.gv[i], dst + TILEB);
             }
@@ -297,23 +319,30 @@ struct Kernel {
                 const int key = min(tr.key0 + S.krow[i], tr.nk - 1);
                 // gk holds krow rows; move the lane to row key - b0
                 const unsigned adj = (unsigned)((key - b0 - S.krow[i]) * (int)S.kstride * 2);
-                const unsigned dst = sK + (wave * KI + i) * 4 * ROWB;
+                const unsigned dst = sK + (wave * KI + i) * RPC * ROWB;
                 dma16(kb, S.gk[i] + adj, dst);
                 dma16(vb, S.gv[i] + adj, dst + TILEB);
             }
         }
     }
 
+    // The O^T products of matrix step i: products 2i and 2i+1 of the
+    // (key chunk, head-dim tile) pairs in chunk-major order.
+    __device__ __forceinline__ static constexpr int o_chunk(int i, int j) {
+        return (2 * i + j) / (D / 32);
+    }
+    __device__ __forceinline__ static constexpr int o_tile(int i, int j) {
+        return (2 * i + j) % (D / 32);
+    }
     // LDS operands of matrix step i (see matrix_phase): the two K chunks of
-    // k-step i and the two V^T blocks of head-dim tiles 2(i%2), 2(i%2)+1 of
-    // key chunk i/2.
+    // k-step i and the V^T blocks of its two O^T products.
     __device__ __forceinline__ static void step_reads(const State &S, int i, bf16x8 (&kf)[2],
                                                       bf16x8 (&vf)[2]) {
         kf[0] = k_read(S.koff[i]);
         kf[1] = k_read(S.koff[i] + 32 * ROWB);
-        const int kc = i >> 1, dt0 = 2 * (i & 1);
-        vf[0] = vt_read(S.voff[dt0] + kc * 16 * ROWB);
-        vf[1] = vt_read(S.voff[dt0 + 1] + kc * 16 * ROWB);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            vf[j] = vt_read<ROWB>(S.voff[o_tile(i, j)] + o_chunk(i, j) * 16 * ROWB);
     }
 
     // The operands of the first two matrix steps, read ahead: a wave issues
@@ -334,8 +363,10 @@ struct Kernel {
     // tile by P = 0, and the S^T of the phase after a wave's last tile is
     // computed on resident rows and dropped.
     __device__ __forceinline__ static void matrix_phase(State &S, const Ahead &A) {
-        // Eight steps of four MFMAs: step i does k-step i of S^T (both 32-key
-        // halves) and head-dim tiles 2(i%2), 2(i%2)+1 of key chunk i/2 of O^T.
+        // D/16 steps of four MFMAs: step i does k-step i of S^T (both 32-key
+        // halves) and O^T products 2i and 2i+1 (chunk-major order: for D = 128
+        // head-dim tiles 2(i%2), 2(i%2)+1 of key chunk i/2; for D = 64 both
+        // tiles of key chunk i).
         // The LDS reads of step i+2 are issued before the MFMAs of step i, so
         // two steps of matrix work cover each read's latency (the fences keep
         // the compiler from hoisting every read, which would exhaust registers).
@@ -348,9 +379,9 @@ struct Kernel {
             vf[1][j] = A.vf[1][j];
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NSTEP; ++i) {
             const int cur = i % 3;
-            if (i + 2 < 8) step_reads(S, i + 2, kf[(i + 2) % 3], vf[(i + 2) % 3]);
+            if (i + 2 < NSTEP) step_reads(S, i + 2, kf[(i + 2) % 3], vf[(i + 2) % 3]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
@@ -358,11 +389,10 @@ struct Kernel {
                                        kf[cur][h2], S.qf[i], f32x16{}, 0, 0, 0)
                                  : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                                        kf[cur][h2], S.qf[i], S.s[h2], 0, 0, 0);
-            const int kc = i >> 1, dt0 = 2 * (i & 1);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                S.acc[dt0 + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][j], S.pf[kc],
-                                                                         S.acc[dt0 + j], 0, 0, 0);
+                S.acc[o_tile(i, j)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    vf[cur][j], S.pf[o_chunk(i, j)], S.acc[o_tile(i, j)], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -488,11 +518,11 @@ struct Kernel {
         S.kstride = (int64_t)p.hkv * D;
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
-            const int row = (wave * KI + i) * 4 + (lane >> 4);
-            const int phys = lane & 15;
+            const int row = (wave * KI + i) * RPC + lane / CPR;
+            const int phys = lane % CPR;
             S.krow[i] = row;
-            S.gk[i] = (unsigned)(row * S.kstride * 2 + ((phys ^ (swap_bits23(row) & 15)) << 4));
-            S.gv[i] = (unsigned)(row * S.kstride * 2 + ((phys ^ ((row & 3) << 2)) << 4));
+            S.gk[i] = (unsigned)(row * S.kstride * 2 + ((phys ^ k_swz(row)) << 4));
+            S.gv[i] = (unsigned)(row * S.kstride * 2 + ((phys ^ v_swz(row)) << 4));
         }
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
@@ -514,15 +544,17 @@ struct Kernel {
 
         {
             const int krow = swap_bits23(l32);             // K row fed to matrix row l32
+            const int ksw = D == 128 ? (l32 & 15) : k_swz(krow);   // k_swz(krow)
 #pragma unroll
             for (int kk = 0; kk < D / 16; ++kk)
-                S.koff[kk] = krow * ROWB + (((kk * 2 + hi) ^ (l32 & 15)) << 4);
+                S.koff[kk] = krow * ROWB + (((kk * 2 + hi) ^ ksw) << 4);
             const int vg = lane >> 4, vj = (lane >> 2) & 3, vq = lane & 3;
             const int x = 2 * (vg & 1) + (vq >> 1);
+            const int vrow = 8 * (vg >> 1) + vj;
+            const int vsw = D == 128 ? vj << 2 : v_swz(vrow);         // v_swz(vrow)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
-                S.voff[dt] = (8 * (vg >> 1) + vj) * ROWB + (((dt * 4 + x) ^ (vj << 2)) << 4) +
-                             (vq & 1) * 8;
+                S.voff[dt] = vrow * ROWB + (((dt * 4 + x) ^ vsw) << 4) + (vq & 1) * 8;
         }
         const unsigned lds_addr =
             (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
@@ -632,11 +664,11 @@ struct Kernel {
 };
 
 // One CP step (fp32 partial output).
-template <bool CAUSAL>
+template <bool CAUSAL, int D>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_step_bf16(Params p) {
-    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
-    Kernel<StepPlan<CAUSAL>, false>::run(p, lds);
+    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * tile_bytes(D)];
+    Kernel<StepPlan<CAUSAL, D>, false>::run(p, lds);
 }
 
 // Several CP steps of one rank in one launch (fp32 partial outputs).  The
@@ -670,6 +702,7 @@ struct StepsParams {
 };
 static_assert(sizeof(StepsParams) <= 4096, "kernel arguments");
 
+template <int D>
 __device__ __forceinline__ void steps_item(const StepsParams &sp, int item, char *lds) {
     const int ng = item / sp.items;
     int w = item - ng * sp.items;
@@ -696,18 +729,19 @@ __device__ __forceinline__ void steps_item(const StepsParams &sp, int item, char
     const int hh = w % sp.group, qt = r.qt0 + r.dir * (w / sp.group);
     const int g = ng % sp.hkv, n = ng / sp.hkv;
     if (d.causal)
-        Kernel<StepPlan<true>, false>::run_item(p, lds, n, g, hh, qt);
+        Kernel<StepPlan<true, D>, false>::run_item(p, lds, n, g, hh, qt);
     else
-        Kernel<StepPlan<false>, false>::run_item(p, lds, n, g, hh, qt);
+        Kernel<StepPlan<false, D>, false>::run_item(p, lds, n, g, hh, qt);
 }
 
+template <int D>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_steps_bf16(StepsParams sp) {
-    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
+    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * tile_bytes(D)];
     // workgroup -> (batch, KV head), then the run, then (query tile, head in
     // group) inside it; the runs are laid out longest first across all steps
     if (sp.total == (int)gridDim.x) {
-        steps_item(sp, xcd_order(blockIdx.x, gridDim.x), lds);
+        steps_item<D>(sp, xcd_order(blockIdx.x, gridDim.x), lds);
         return;
     }
     // Fewer workgroups than items (one per CU, a multiple of 8 of each):
@@ -722,16 +756,16 @@ attn_steps_bf16(StepsParams sp) {
         const int li = r * nslot + ((r & 1) ? nslot - 1 - slot : slot);
         if (li >= range) continue;
         if (r > 0) lds_barrier();   // every wave is done with the LDS of the last item
-        steps_item(sp, xq * range + li, lds);
+        steps_item<D>(sp, xq * range + li, lds);
     }
 }
 
 // A rank's whole share (merged output, fp32 or bf16).
-template <bool OUT_BF16>
+template <bool OUT_BF16, int D>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fused_bf16(Params p) {
-    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * TILEB];
-    Kernel<FusedPlan, OUT_BF16>::run(p, lds);
+    __shared__ __attribute__((aligned(1024))) char lds[NS * 2 * tile_bytes(D)];
+    Kernel<FusedPlan<D>, OUT_BF16>::run(p, lds);
 }
 
 template <class KernelFn>
@@ -760,8 +794,12 @@ hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, con
     p.group = g.hq / g.hkv;
     p.num_qtiles = (int)((g.nq + BM - 1) / BM);
     p.scale_log2 = g.scale_log2;
-    if (g.causal) return launch_kernel(attn_step_bf16<true>, p, g.b, g.hq, stream);
-    return launch_kernel(attn_step_bf16<false>, p, g.b, g.hq, stream);
+    if (g.d == 64) {
+        if (g.causal) return launch_kernel(attn_step_bf16<true, 64>, p, g.b, g.hq, stream);
+        return launch_kernel(attn_step_bf16<false, 64>, p, g.b, g.hq, stream);
+    }
+    if (g.causal) return launch_kernel(attn_step_bf16<true, 128>, p, g.b, g.hq, stream);
+    return launch_kernel(attn_step_bf16<false, 128>, p, g.b, g.hq, stream);
 }
 
 int device_cu_count() {
@@ -849,14 +887,19 @@ hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void
     // CU and the items split evenly over the 8 XCD ranges
     const int64_t slots = resident_slots();
     const int64_t blocks = (slots >= 8 && total % 8 == 0 && total > 2 * slots) ? slots : total;
-    hipLaunchKernelGGL(attn_steps_bf16, dim3((unsigned)blocks), dim3(64 * NW), 0, stream, sp);
+    if (g[0].d == 64)
+        hipLaunchKernelGGL(attn_steps_bf16<64>, dim3((unsigned)blocks), dim3(64 * NW), 0, stream,
+                           sp);
+    else
+        hipLaunchKernelGGL(attn_steps_bf16<128>, dim3((unsigned)blocks), dim3(64 * NW), 0, stream,
+                           sp);
     return hipGetLastError();
 }
 
 hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz, const void *vz,
                              void *o, bool out_bf16, float *lse, hipStream_t stream) {
     Params p = {};
-    const int64_t block_q = f.b * f.two_c * f.hq * D;     // one rank's Q block, elements
+    const int64_t block_q = f.b * f.two_c * f.hq * f.d;   // one rank's Q block, elements
     p.q = (const uint16_t *)qz + f.rank * block_q;
     p.k = (const uint16_t *)kz;
     p.v = (const uint16_t *)vz;
@@ -872,15 +915,19 @@ hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
     p.scale_log2 = f.scale_log2;
     p.rank = f.rank;
     p.cp = f.cp;
-    p.block_elems = f.b * f.two_c * f.hkv * D;
+    p.block_elems = f.b * f.two_c * f.hkv * f.d;
     // query tiles sample by sample
     p.tab = f.tab;
     p.tab.tile0[0] = 0;
     for (int i = 0; i < p.tab.nseq; ++i)
         p.tab.tile0[i + 1] = p.tab.tile0[i] + (p.tab.lcu[i + 1] - p.tab.lcu[i] + BM - 1) / BM;
     p.num_qtiles = p.tab.tile0[p.tab.nseq];
-    if (out_bf16) return launch_kernel(attn_fused_bf16<true>, p, f.b, f.hq, stream);
-    return launch_kernel(attn_fused_bf16<false>, p, f.b, f.hq, stream);
+    if (f.d == 64) {
+        if (out_bf16) return launch_kernel(attn_fused_bf16<true, 64>, p, f.b, f.hq, stream);
+        return launch_kernel(attn_fused_bf16<false, 64>, p, f.b, f.hq, stream);
+    }
+    if (out_bf16) return launch_kernel(attn_fused_bf16<true, 128>, p, f.b, f.hq, stream);
+    return launch_kernel(attn_fused_bf16<false, 128>, p, f.b, f.hq, stream);
 }
 
 }  // namespace cpattn

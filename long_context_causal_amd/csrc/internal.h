@@ -72,14 +72,14 @@ hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void
 struct FusedGeom {
     int64_t b;
     int64_t two_c;      // local rows per batch element (s / cp)
-    int32_t hq, hkv, rank, cp;
+    int32_t hq, hkv, d, rank, cp;
     float scale_log2;
     SeqTable tab;       // the packed samples (tile0 filled by the launcher)
 };
 
-// qz, kz, vz: the partitioned tensors of all ranks [cp, b, s/cp, h, 128]
-// bf16.  o: [b, s/cp, hq, 128] fp32, or bf16 when out_bf16; lse:
-// [b, hq, s/cp] or null.
+// qz, kz, vz: the partitioned tensors of all ranks [cp, b, s/cp, h, d]
+// bf16 (d = 64 or 128).  o: [b, s/cp, hq, d] fp32, or bf16 when out_bf16;
+// lse: [b, hq, s/cp] or null.
 hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
                              const void *vz, void *o, bool out_bf16, float *lse,
                              hipStream_t stream);

@@ -43,11 +43,13 @@ __device__ __forceinline__ bf16x8 k_read(unsigned addr) {
 // L = 16*g + 4*j + q reads, for s in {0, 1}, the 8-byte block at tile row
 // kc*16 + 8*(g/2) + 4*s + j, head dims dt*32 + 16*(g%2) + 4*q .. +3; the
 // transpose hands lane t of group g the column dt*32 + 16*(g%2) + t for rows
-// +0..3 of that row block.  addr: row 8*(g/2) + j of the tile's dims block.
+// +0..3 of that row block.  addr: row 8*(g/2) + j of the tile's dims block;
+// RB: bytes per tile row.
+template <int RB = ROW_BYTES>
 __device__ __forceinline__ bf16x8 vt_read(unsigned addr) {
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)addr);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4 *)(uintptr_t)(addr + 4 * ROW_BYTES));
+        (lds_s16x4 *)(uintptr_t)(addr + 4 * RB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 

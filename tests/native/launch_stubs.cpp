@@ -50,7 +50,7 @@ hipError_t launch_partition(const cpattn_dims &dims, int dtype, int h, const Seq
 hipError_t launch_step_bf16(const StepGeom &g, const void *q, const void *k, const void *v,
                             float *o, float *lse, hipStream_t) {
     check_geom(g);
-    REQUIRE(q && k && v && o && lse && g.d == 128);
+    REQUIRE(q && k && v && o && lse && (g.d == 64 || g.d == 128));
     ++stubs::launches[stubs::STEP_BF16];
     return hipSuccess;
 }
@@ -70,7 +70,7 @@ hipError_t launch_steps_bf16(int n, const StepGeom *g, const void *q, const void
 hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz, const void *vz,
                              void *o, bool, float *, hipStream_t) {
     check_table(f.tab);
-    REQUIRE(qz && kz && vz && o && f.rank >= 0 && f.rank < f.cp);
+    REQUIRE(qz && kz && vz && o && f.rank >= 0 && f.rank < f.cp && (f.d == 64 || f.d == 128));
     ++stubs::launches[stubs::FUSED];
     return hipSuccess;
 }

@@ -24,6 +24,19 @@ ONE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp1",
                              hkv=2, cp=1)
 EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP}
 
+# 64-wide heads (the pages fix no head dimension): GQA, MHA with wide
+# logits, RoPE at global positions; ragged chunks
+HEAD64 = {
+    "gqa": dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_d64_cp4",
+                               s=2 * 4 * 100, hq=8, hkv=2, d=64),
+    "mha_wide": dataclasses.replace(WORKLOADS["bf16_mha_s16k_cp4_widelogits"],
+                                    name="bf16_mha_d64_cp4_widelogits", s=2 * 4 * 96, hq=4,
+                                    hkv=4, d=64),
+    "rope_cp8": dataclasses.replace(WORKLOADS["bf16_gqa_s128k_cp16_rope"],
+                                    name="bf16_gqa_d64_cp8_rope", s=2 * 8 * 72, hq=8, hkv=2,
+                                    d=64, cp=8),
+}
+
 
 REDUCED = [("fp32_mha_s512_cp2", 2 * 2 * 77, None),
            ("bf16_gqa_s8k_cp4", 2 * 4 * 100, None),
@@ -68,6 +81,29 @@ def test_forward_extreme_cp_all_ranks(name):
         pos = ocp.zigzag_positions(w.s, w.cp, r)
         assert_close(f"rank {r} O", o, o_full[:, pos], BF16_MAX_ABS, BF16_MEAN_ABS)
         assert_close(f"rank {r} L", l, l_full[:, :, pos], 1e-3)
+
+
+@pytest.mark.parametrize("name", sorted(HEAD64))
+def test_forward_head_dim_64_all_ranks(name):
+    """bf16 with d = 64: every rank through cpattn_forward (steps grid and
+    merge) and through cpattn_forward_fused, vs the oracle."""
+    w = HEAD64[name]
+    say(f"forward d=64 {w.name} s={w.s} cp={w.cp}")
+    q, k, v = make_inputs(w)
+    o_full, l_full = oracle_full(w, q, k, v)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    for r in range(w.cp):
+        pos = ocp.zigzag_positions(w.s, w.cp, r)
+        o, l = run_rank(P, r)
+        assert_close(f"rank {r} O", o, o_full[:, pos], BF16_MAX_ABS, BF16_MEAN_ABS)
+        assert_close(f"rank {r} L", l, l_full[:, :, pos], 1e-3)
+        out = P.alloc_out(r, C.CPATTN_F32)
+        P.forward_fused(out)
+        torch.cuda.synchronize()
+        assert_close(f"rank {r} fused O", out["o"].cpu().numpy(), o_full[:, pos], BF16_MAX_ABS,
+                     BF16_MEAN_ABS)
+        assert_close(f"rank {r} fused L", out["lse"].cpu().numpy(), l_full[:, :, pos], 1e-3)
 
 
 @pytest.mark.parametrize("cp", [128, 256])

@@ -62,6 +62,20 @@ def test_step_bf16(mode, b, c, hq, hkv, qk):
     assert_close("L", l, l_ref, 1e-3)
 
 
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("b,c,hq,hkv,qk", [(1, 256, 8, 2, 0.5),    # whole tiles
+                                           (2, 100, 4, 4, 1.0),    # ragged query and key tiles
+                                           (1, 37, 8, 1, 1.0),     # tiny, MQA
+                                           (1, 300, 2, 2, 2.24)])  # logits ~ +-30
+def test_step_bf16_head_dim_64(mode, b, c, hq, hkv, qk):
+    """The bf16 kernel built for 64-wide heads (128-byte LDS rows, eight rows
+    per copy, its own swizzles, four matrix steps per phase)."""
+    o, l, o_ref, l_ref = _run_step("bf16", mode, b, c, hq, hkv, 64, seed=11 * c + mode,
+                                   qk_scale=qk)
+    assert_close("O", o, o_ref, BF16_MAX_ABS, BF16_MEAN_ABS)
+    assert_close("L", l, l_ref, 1e-3)
+
+
 def test_step_explicit_scale():
     o, l, o_ref, l_ref = _run_step("bf16", C.CPATTN_CAUSAL, 1, 64, 2, 2, 128, seed=3,
                                    scale=0.02)

@@ -105,12 +105,17 @@ FUSED = [("bf16_gqa_s8k_cp4", [100, 1, 37, 256, 64], None),
          ("bf16_gqa_s128k_cp16_rope", [24, 7, 65], None)]
 
 
-@pytest.mark.parametrize("name,chunks,b", FUSED)
-def test_fused_varlen_reduced_all_ranks(name, chunks, b):
-    base = WORKLOADS[name]
+# 64-wide heads (GQA, and RoPE at in-sample positions)
+FUSED_D64 = [("bf16_gqa_s8k_cp4", [100, 1, 37, 256, 64], None, 64),
+             ("bf16_gqa_s128k_cp16_rope", [24, 7, 65], None, 64)]
+
+
+@pytest.mark.parametrize("name,chunks,b,d", [f + (128,) for f in FUSED] + FUSED_D64)
+def test_fused_varlen_reduced_all_ranks(name, chunks, b, d):
+    base = dataclasses.replace(WORKLOADS[name], d=d)
     cu = _cu(base.cp, chunks)
     w = small(base, int(cu[-1]), b)
-    say(f"fused varlen {name} cu={cu.tolist()} b={w.b}")
+    say(f"fused varlen {name} cu={cu.tolist()} b={w.b} d={w.d}")
     q, k, v = make_inputs(w)
     o_ref, l_ref = _packed_ref(w, q, k, v, cu)
     P = CPProblem(w, q, k, v, cu_seqlens=cu)

@@ -365,7 +365,10 @@ def digest(prof_dir):
         win = windows(rows)
         lo, hi = (win["c5"], 1 << 62) if w_name == "bf16_gqa_s128k_cp16_rope" else (
             0, win["per_step"])
-        sel = sorted((r for r in rows if _short_kernel(r["Kernel_Name"]) == "attn_steps_bf16"
+        # the grid kernel is a template over the head dimension (d = 128 here)
+        sel = sorted((r for r in rows
+                      if _short_kernel(r["Kernel_Name"]) in ("attn_steps_bf16",
+                                                             "attn_steps_bf16<128>")
                       and lo <= int(r["Dispatch_Id"]) < hi), key=lambda r: int(r["Dispatch_Id"]))
         return [value(r) for r in (sel[-last:] if last else sel)]
 

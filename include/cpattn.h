@@ -55,7 +55,7 @@ typedef struct cpattn_dims {
     int64_t s;    /* full sequence length, a multiple of 2*cp                 */
     int32_t hq;   /* query heads, a multiple of hkv                           */
     int32_t hkv;  /* key/value heads (GQA groups)                              */
-    int32_t d;    /* head dimension: 64 or 128 (the bf16 backward: 128 only) */
+    int32_t d;    /* head dimension: 64 or 128                                */
     int32_t cp;   /* context-parallel size (ranks emulated), >= 1: any cp with
                      s % (2*cp) == 0, down to chunks of one row (c = 1)       */
 } cpattn_dims;
@@ -267,11 +267,11 @@ int cpattn_forward_fused(const cpattn_dims *dims, int dtype, float scale, int ra
  *
  * cpattn_bwd_delta, device: delta_r [b, hq, 2c] fp32 = sum over the head
  * dim of do_r [b, 2c, hq, d] (bf16) times o_r [b, 2c, hq, d] (fp32, the
- * merged forward output).  d = 128. */
+ * merged forward output).  d = 64 or 128. */
 int cpattn_bwd_delta(const cpattn_dims *dims, const float *o_r, const void *do_r,
                      float *delta_r, void *stream);
 
-/* cpattn_step_bwd, device: one step's backward (CPATTN_BF16 only, d = 128).
+/* cpattn_step_bwd, device: one step's backward (CPATTN_BF16 only, d = 64 or 128).
  * q_r, do_r [b, 2c, hq, d] bf16; k_src, v_src [b, 2c, hkv, d] bf16 (rank
  * src's blocks); lse_r, delta_r [b, hq, 2c] fp32.  For each row i and head h
  * of the mode and each key j it lets them see, with P = exp(scale q.k - L)

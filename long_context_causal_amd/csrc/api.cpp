@@ -463,12 +463,11 @@ int cpattn_bwd_delta(const cpattn_dims *dims, const float *o_r, const void *do_r
     int st = check_dims(dims);
     if (st) return st;
     if (!o_r || !do_r || !delta_r) return CPATTN_EINVAL;
-    if (dims->d != 128) return CPATTN_ESHAPE;
     if (!aligned16(o_r) || !aligned16(do_r) || ((uintptr_t)delta_r & 3u)) return CPATTN_EALIGN;
     const int64_t two_c = dims->s / dims->cp;
     if (!fits_grid(dims->b * two_c * dims->hq / 256 + 1)) return CPATTN_ESHAPE;
-    return status_of(cpattn::launch_bwd_delta(dims->b, two_c, dims->hq, o_r, do_r, delta_r,
-                                              (hipStream_t)stream));
+    return status_of(cpattn::launch_bwd_delta(dims->b, two_c, dims->hq, dims->d, o_r, do_r,
+                                              delta_r, (hipStream_t)stream));
 }
 
 int cpattn_step_bwd(const cpattn_dims *dims, int dtype, float scale, int mode, const void *q_r,
@@ -482,7 +481,6 @@ int cpattn_step_bwd(const cpattn_dims *dims, int dtype, float scale, int mode, c
         return CPATTN_EINVAL;
     if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
     if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
-    if (dims->d != 128) return CPATTN_ESHAPE;
     if (!aligned16(q_r) || !aligned16(k_src) || !aligned16(v_src) || !aligned16(do_r) ||
         !aligned16(dq_r) || !aligned16(dk_src) || !aligned16(dv_src) ||
         ((uintptr_t)lse_r & 3u) || ((uintptr_t)delta_r & 3u))
@@ -513,7 +511,6 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
         return CPATTN_EINVAL;
     if (!(scale == scale) || isinf(scale)) return CPATTN_EINVAL;
     if (dtype != CPATTN_BF16) return CPATTN_EDTYPE;
-    if (dims->d != 128) return CPATTN_ESHAPE;
     if (!aligned16(qz) || !aligned16(kz) || !aligned16(vz) || !aligned16(o_r) ||
         !aligned16(do_r) || !aligned16(dq_r) || !aligned16(dkz) || !aligned16(dvz) ||
         ((uintptr_t)lse_r & 3u) || ((uintptr_t)delta_ws & 3u))
@@ -550,8 +547,8 @@ int cpattn_backward_varlen(const cpattn_dims *dims, int dtype, float scale, int 
     hipError_t e = cpattn::launch_fill_zero(dkz, kv_elems * dims->cp, s);
     if (e == hipSuccess) e = cpattn::launch_fill_zero(dvz, kv_elems * dims->cp, s);
     if (e == hipSuccess)
-        e = cpattn::launch_bwd_prep(dims->b, two_c, dims->hq, o_r, do_r, lse_r, inv_scale, nl,
-                                    nd, s);
+        e = cpattn::launch_bwd_prep(dims->b, two_c, dims->hq, dims->d, o_r, do_r, lse_r,
+                                    inv_scale, nl, nd, s);
     if (e != hipSuccess) return CPATTN_EHIP;
     // every step's dq in one grid (a workgroup streams all steps' keys for
     // its query rows and writes dq once), then every step's dK/dV in one

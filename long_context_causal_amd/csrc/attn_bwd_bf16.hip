@@ -50,11 +50,19 @@ namespace {
 
 using namespace tiles;
 
-constexpr int D = 128;
 constexpr int TR = 32;                     // rows of a streamed tile; rows (keys) per wave
-constexpr int RB = ROW_BYTES;              // bytes per tile row
-constexpr int TB = TR * RB;                // bytes per tile
 constexpr float LOG2E = 1.4426950408889634f;
+// Tile geometry for head dimension D (bf16 rows of D): bytes per tile row and
+// per tile, and the 1 KB copies (64 lanes x 16 bytes) of a tile.
+template <int D>
+struct TileGeo {
+    static_assert(D == 64 || D == 128, "head dimension");
+    static constexpr int RB = 2 * D;          // bytes per tile row
+    static constexpr int TB = TR * RB;        // bytes per tile
+    static constexpr int CPR = RB / 16;       // 16-byte chunks per row
+    static constexpr int RPC = 64 / CPR;      // rows per copy
+    static constexpr int NCOPY = TR / RPC;    // copies per tile
+};
 
 struct BwdParams {
     const uint16_t *q, *k, *v, *dout;   // q_r, dout_r [b, T, hq, d]; k, v [b, T, hkv, d]
@@ -91,6 +99,13 @@ __device__ __forceinline__ Geo geo_of(const BwdParams &p, int i, int mode) {
 }
 
 __device__ __forceinline__ int u_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// The same for 128-byte rows (D = 64: 8 chunks, two rows per pass over the
+// 64 banks): chunk c of row r sits at c ^ h_swz(r), h_swz(r) = 4 (r/2 mod 2)
+// + (r/4 mod 4).  A row-chunk read's 16 lanes (rows swap_bits23(0..15) or
+// 16..31) cover the 8 chunk slots of each row parity once; a transposed
+// read's 32 lanes take rows 4s + 0..3 (+8), whose two rows of one parity
+// fall in opposite halves of the row.
+__device__ __forceinline__ int h_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // The lane's LDS byte offsets in a swizzled tile, kept as a few bases and
 // XOR masks (the swizzle is an XOR, so each offset is one v_xad):
@@ -100,7 +115,9 @@ __device__ __forceinline__ int u_swz(int r) { return ((r & 3) << 2) | ((r >> 2) 
 //   chunk 4 dt + x, byte 8 (lane & 1)): tb[s] + 64 (dt ^ (f' >> 2)), where
 //   f' = u_swz(row) (rows +0 and +4 differ only in bit 0 of f');
 // add kc * 16 * RB for the second 16-row chunk, which has the same swizzle.
+template <int D>
 struct LaneOffsets {
+    static constexpr int RB = TileGeo<D>::RB;
     unsigned rbase, rmask, tb[2], tmask;
     __device__ __forceinline__ void init(int lane) {
         const int hi = lane >> 5, l32 = lane & 31;
@@ -122,6 +139,24 @@ struct LaneOffsets {
         return ((dt << 6) ^ tmask) + tb[s];
     }
 };
+// 128-byte rows: the offsets written out (the lane's row and chunk as for
+// 256-byte rows, the h_swz swizzle).
+template <>
+struct LaneOffsets<64> {
+    static constexpr int RB = TileGeo<64>::RB;
+    int lane_;
+    __device__ __forceinline__ void init(int lane) { lane_ = lane; }
+    __device__ __forceinline__ unsigned roff(int kk) const {
+        const int hi = lane_ >> 5, r = swap_bits23(lane_ & 31);
+        return (unsigned)(r * RB + (((2 * kk + hi) ^ h_swz(r)) << 4));
+    }
+    __device__ __forceinline__ unsigned toff(int dt, int s) const {
+        const int vg = lane_ >> 4, vj = (lane_ >> 2) & 3, vq = lane_ & 3;
+        const int x = 2 * (vg & 1) + (vq >> 1);
+        const int row = 8 * (vg >> 1) + 4 * s + vj;
+        return (unsigned)(row * RB + (((4 * dt + x) ^ h_swz(row)) << 4) + (vq & 1) * 8);
+    }
+};
 
 // Transposed operand from two row blocks (see vt_read).
 __device__ __forceinline__ bf16x8 vt_read2(unsigned a0, unsigned a1) {
@@ -135,13 +170,22 @@ __device__ __forceinline__ bf16x8 vt_read2(unsigned a0, unsigned a1) {
 // chunk L%16, so it loads chunk (L%16) ^ u_swz(row) of that row.  Returns
 // the lane's byte offset from the copy's first row; u_swz(row) depends on m
 // only through m % 4.
+// With 128-byte rows (D = 64) a copy is 8 rows: lane L lands on row 8m + L/8,
+// chunk L%8, and loads chunk (L%8) ^ h_swz(row).
+template <int D>
 __device__ __forceinline__ unsigned copy_offset(int lane, int m, int64_t row_bytes) {
-    const int r = lane >> 4;
-    return (unsigned)(r * row_bytes) + ((((lane & 15) ^ ((r << 2) | (m & 3)))) << 4);
+    if constexpr (D == 64) {
+        const int r = lane >> 3;
+        return (unsigned)(r * row_bytes) + (((lane & 7) ^ h_swz(8 * m + r)) << 4);
+    } else {
+        const int r = lane >> 4;
+        return (unsigned)(r * row_bytes) + ((((lane & 15) ^ ((r << 2) | (m & 3)))) << 4);
+    }
 }
 
-// B operand of the 8 k-steps for one row (this lane's l32-th row of a
+// B operand of the D/16 k-steps for one row (this lane's l32-th row of a
 // 32-row block): row chunks kk*16 + 8*hi .. +7.
+template <int D>
 __device__ __forceinline__ void load_b_rows(const uint16_t *row, int hi, bf16x8 (&f)[D / 16]) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
@@ -169,19 +213,21 @@ __device__ __forceinline__ unsigned pin(unsigned x) {
 
 #define MFMA __builtin_amdgcn_mfma_f32_32x32x16_bf16
 
-// Issues one wave's copies of rows [4 m, 4 m + 4) of a 32-row tile whose
-// first row is row0 (of n rows; rows past n repeat row n-1) from the row
-// array base (row stride row_bytes) into the stage tile at sdst.  off: the
-// lane's copy_offset for m.
+// Issues one wave's copy m of a 32-row tile (rows [RPC m, RPC m + RPC))
+// whose first row is row0 (of n rows; rows past n repeat row n-1) from the
+// row array base (row stride row_bytes) into the stage tile at sdst.  off:
+// the lane's copy_offset for m.
+template <int D>
 __device__ __forceinline__ void copy_rows(const uint16_t *base, int64_t row_bytes, int row0,
                                           int n, int m, unsigned off, unsigned sdst, int lane) {
+    constexpr int RPC = TileGeo<D>::RPC;
     if (row0 + TR <= n) {
-        dma16((const char *)base + (row0 + 4 * m) * row_bytes, off, sdst + m * 1024);
+        dma16((const char *)base + (row0 + RPC * m) * row_bytes, off, sdst + m * 1024);
     } else {
         // base row b0 <= every row copied, so lane offsets stay >= 0
         const int b0 = max(min(row0, n - TR), 0);
-        const int r = lane >> 4;
-        const int row = min(row0 + 4 * m + r, n - 1);
+        const int r = lane / (64 / RPC);
+        const int row = min(row0 + RPC * m + r, n - 1);
         const unsigned o = off + (unsigned)((row - b0 - r) * row_bytes);
         dma16((const char *)base + b0 * row_bytes, o, sdst + m * 1024);
     }
@@ -197,7 +243,8 @@ __device__ __forceinline__ void copy_rows(const uint16_t *base, int64_t row_byte
 constexpr int NWB = 4;                     // waves of the single step's dq
 constexpr int NSQ = 4;
 constexpr int PDQ = NSQ - 1;
-constexpr int STAGE_DQ = 2 * TB;           // K, V
+template <int D>
+constexpr int stage_dq() { return 2 * TileGeo<D>::TB; }   // K, V
 
 // A cursor over the 32-key tiles a dQ workgroup streams for its query rows,
 // one step per tile: the K, V base of the current key block (this batch
@@ -213,7 +260,9 @@ struct DqCursor {
 
 // One step (cpattn_step_bwd's dq launch): the sample's rows and keys of the
 // step's mode, one block.
+template <int D>
 struct DqStepPlan {
+    static constexpr int kD = D;
     const uint16_t *kb, *vb;
     int qrow0, nq, nk, ntiles;
     bool causal;
@@ -243,7 +292,9 @@ struct DqStepPlan {
 // [0, 2c) of ranks cp-1 .. r+1, seen by rows c .. 2c-1 only; streamed only
 // when the tile has such rows), then step 0 (the rank's own block,
 // causal).  dQ of every step sums in the same accumulator.
+template <int D>
 struct DqSharePlan {
+    static constexpr int kD = D;
     const uint16_t *k0, *v0;
     int64_t block;
     int r, cp, c, nAB, kend, ntiles;
@@ -298,7 +349,11 @@ struct DqSharePlan {
 // of L and D.
 template <class Plan, bool ACCUMULATE, bool PREP, int NW>
 __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
-    constexpr int CPW = 8 / NW;   // 4-row copies per wave and tensor per tile
+    constexpr int D = Plan::kD;
+    constexpr int RB = TileGeo<D>::RB, TB = TileGeo<D>::TB, RPC = TileGeo<D>::RPC;
+    constexpr int STAGE_DQ = stage_dq<D>();
+    constexpr int CPW = TileGeo<D>::NCOPY / NW;   // copies per wave and tensor per tile
+    static_assert(CPW >= 1 && CPW * NW == TileGeo<D>::NCOPY, "copy split");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5, l32 = lane & 31;
@@ -326,7 +381,7 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
     P.init(p, smp, q0, n, g, TR * NW);
     const int ntiles = P.ntiles;
 
-    LaneOffsets L;
+    LaneOffsets<D> L;
     L.init(lane);
     const unsigned lbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
 
@@ -335,8 +390,8 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
     const int qr = min(qrow, P.nq - 1);
     const int64_t qoff = ((n * p.two_c + P.qrow0 + qr) * (int64_t)p.hq + head) * D;
     bf16x8 qf[D / 16], df[D / 16];
-    load_b_rows(p.q + qoff, hi, qf);
-    load_b_rows(p.dout + qoff, hi, df);
+    load_b_rows<D>(p.q + qoff, hi, qf);
+    load_b_rows<D>(p.dout + qoff, hi, df);
     const int64_t lrow = ((int64_t)n * p.hq + head) * p.two_c + P.qrow0 + qr;
     const float lq = PREP ? -p.lse[lrow] * p.scale_log2 : p.lse[lrow] * LOG2E;
     const float dq_d = PREP ? -p.delta[lrow] : p.delta[lrow];
@@ -351,7 +406,7 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
         for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
 
     const int64_t row_bytes = (int64_t)p.hkv * D * 2;
-    const unsigned coff = copy_offset(lane, wave, row_bytes);   // m = wave (+ NW)
+    const unsigned coff = copy_offset<D>(lane, wave, row_bytes);   // m = wave (+ NW)
     // copy cursor (tile cu); tiles past the last repeat it, so every wave
     // issues 2 CPW copies per tile
     DqCursor CC = P.first();
@@ -362,15 +417,17 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) {
                 const int m = wave + NW * i;
-                dma16((const char *)CC.kb + (CC.key0 + 4 * m) * row_bytes, coff, sb + m * 1024);
-                dma16((const char *)CC.vb + (CC.key0 + 4 * m) * row_bytes, coff,
+                dma16((const char *)CC.kb + (CC.key0 + RPC * m) * row_bytes, coff,
+                      sb + m * 1024);
+                dma16((const char *)CC.vb + (CC.key0 + RPC * m) * row_bytes, coff,
                       sb + TB + m * 1024);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) {
-                copy_rows(CC.kb, row_bytes, CC.key0, CC.nk, wave + NW * i, coff, sb, lane);
-                copy_rows(CC.vb, row_bytes, CC.key0, CC.nk, wave + NW * i, coff, sb + TB, lane);
+                copy_rows<D>(CC.kb, row_bytes, CC.key0, CC.nk, wave + NW * i, coff, sb, lane);
+                copy_rows<D>(CC.vb, row_bytes, CC.key0, CC.nk, wave + NW * i, coff, sb + TB,
+                             lane);
             }
         }
     };
@@ -498,19 +555,20 @@ __device__ __forceinline__ void dq_body(const BwdParams &p, char *lds) {
 }
 
 // One step's dq (accumulated into dq).
+template <int D>
 __global__ void __launch_bounds__(64 * NWB) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
-    dq_body<DqStepPlan, true, false, NWB>(p, lds);
+    __shared__ __attribute__((aligned(1024))) char lds[NSQ * stage_dq<D>()];
+    dq_body<DqStepPlan<D>, true, false, NWB>(p, lds);
 }
 
 // The dq of all cp steps of a rank's share in one grid: a workgroup streams
 // every step's keys for its query tile and writes dq once.
-template <int NW>
+template <int NW, int D>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq_share(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[NSQ * STAGE_DQ];
-    dq_body<DqSharePlan, false, true, NW>(p, lds);
+    __shared__ __attribute__((aligned(1024))) char lds[NSQ * stage_dq<D>()];
+    dq_body<DqSharePlan<D>, false, true, NW>(p, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -532,9 +590,11 @@ constexpr int KW = 4;                          // key groups of 32 per workgroup
 constexpr int NSK = 5;                         // stages: PDK ahead + the two tiles in use
 constexpr int PDK = NSK - 2;
 constexpr int LD_SLOT = 1024;                  // the tile's L and D (256 bytes used)
-constexpr int STAGE_DKDV = 2 * TB + LD_SLOT;   // Q, dO, L/D
 constexpr int PSLAB = 64 * 16 * 4;             // one key group's fp32 P of a tile
-constexpr int DKDV_LDS = NSK * STAGE_DKDV + 2 * KW * PSLAB;
+template <int D>
+constexpr int stage_dkdv() { return 2 * TileGeo<D>::TB + LD_SLOT; }   // Q, dO, L/D
+template <int D>
+constexpr int dkdv_lds() { return NSK * stage_dkdv<D>() + 2 * KW * PSLAB; }
 
 // What a dK/dV workgroup takes from its step: the source block's K and V,
 // where its dK and dV go, the mode, and over how many workgroups the
@@ -551,9 +611,15 @@ struct KvStep {
 // PREP: p.lse and p.delta hold -L/scale and -D (launch_bwd_prep): they
 // start the sums of S and dP, so that S already holds q.k - L/scale and dP
 // holds dO.v - D.
-template <bool PREP>
+template <bool PREP, int D>
 __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, int item,
                                           char *lds) {
+    constexpr int RB = TileGeo<D>::RB, TB = TileGeo<D>::TB;
+    constexpr int STAGE_DKDV = stage_dkdv<D>();
+    // dS wave cw copies rows 8 cw .. 8 cw + 7 of Q and of dO: CPT copies of
+    // each (two of 4 rows at D = 128, one of 8 at D = 64), and the L/D slot
+    constexpr int CPT = 8 / TileGeo<D>::RPC;
+    constexpr int NCP = 2 * CPT + 1;           // copies per dS wave per tile
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool ds_wave = wave >= KW;           // wave-uniform role
@@ -575,7 +641,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
     const int k0 = kt * TR * KW;
     const int wkey0 = k0 + kwave * TR;
 
-    LaneOffsets L;
+    LaneOffsets<D> L;
     L.init(lane);
     const unsigned lbase = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char *)lds;
 
@@ -584,7 +650,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
     const int kr = min(key, G.nk - 1);
     const int64_t koff = ((n * p.two_c + G.kv0 + kr) * (int64_t)p.hkv + g) * D;
     bf16x8 bf[D / 16];
-    load_b_rows((ds_wave ? io.v : io.k) + koff, hi, bf);
+    load_b_rows<D>((ds_wave ? io.v : io.k) + koff, hi, bf);
     settle(bf);
     f32x16 acc[D / 32];
 #pragma unroll
@@ -704,12 +770,12 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
         const int cw = kwave;   // copies rows 8 cw .. 8 cw + 7 of Q and dO
         const int64_t row_bytes = (int64_t)p.hq * D * 2;
         const int64_t row_step = TR * row_bytes;
-        const unsigned coff0 = copy_offset(lane, 2 * cw, row_bytes);
-        const unsigned coff1 = copy_offset(lane, 2 * cw + 1, row_bytes);
+        const unsigned coff0 = copy_offset<D>(lane, CPT * cw, row_bytes);
+        const unsigned coff1 = copy_offset<D>(lane, CPT * cw + CPT - 1, row_bytes);
         // Copy cursor: tile cu of the workgroup (heads in turn, rows in
         // 32-row tiles), as byte pointers to its first row in Q and dO and
         // the index of that row's L and D.  Tiles past the last repeat it,
-        // so every dS wave issues 5 copies per tile.
+        // so every dS wave issues NCP copies per tile.
         int cu = 0, cr0 = row_first;
         const int64_t hrow0 = (int64_t)n * p.two_c + G.qrow0;   // row of the sample's query 0
         const char *cq = (const char *)(p.q + (hrow0 * p.hq + h0) * D) + row_first * row_bytes;
@@ -723,10 +789,16 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
         auto issue = [&](int stage) {
             const unsigned sb = lbase + stage * STAGE_DKDV;
             if (cr0 + TR <= G.nq) {
-                dma16(cq + 8 * cw * row_bytes, coff0, sb + 2 * cw * 1024);
-                dma16(cq + (8 * cw + 4) * row_bytes, coff1, sb + (2 * cw + 1) * 1024);
-                dma16(cdo + 8 * cw * row_bytes, coff0, sb + TB + 2 * cw * 1024);
-                dma16(cdo + (8 * cw + 4) * row_bytes, coff1, sb + TB + (2 * cw + 1) * 1024);
+                if constexpr (CPT == 2) {
+                    dma16(cq + 8 * cw * row_bytes, coff0, sb + 2 * cw * 1024);
+                    dma16(cq + (8 * cw + 4) * row_bytes, coff1, sb + (2 * cw + 1) * 1024);
+                    dma16(cdo + 8 * cw * row_bytes, coff0, sb + TB + 2 * cw * 1024);
+                    dma16(cdo + (8 * cw + 4) * row_bytes, coff1,
+                          sb + TB + (2 * cw + 1) * 1024);
+                } else {
+                    dma16(cq + 8 * cw * row_bytes, coff0, sb + cw * 1024);
+                    dma16(cdo + 8 * cw * row_bytes, coff0, sb + TB + cw * 1024);
+                }
                 dma4(ld_lane + cli, sb + 2 * TB);
             } else {
                 // the last tile of a head crosses the sample's last row: rows
@@ -734,10 +806,12 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                 const int64_t back = (int64_t)cr0 * row_bytes;
                 const uint16_t *qb = (const uint16_t *)(cq - back);
                 const uint16_t *db = (const uint16_t *)(cdo - back);
-                copy_rows(qb, row_bytes, cr0, G.nq, 2 * cw, coff0, sb, lane);
-                copy_rows(qb, row_bytes, cr0, G.nq, 2 * cw + 1, coff1, sb, lane);
-                copy_rows(db, row_bytes, cr0, G.nq, 2 * cw, coff0, sb + TB, lane);
-                copy_rows(db, row_bytes, cr0, G.nq, 2 * cw + 1, coff1, sb + TB, lane);
+                copy_rows<D>(qb, row_bytes, cr0, G.nq, CPT * cw, coff0, sb, lane);
+                copy_rows<D>(db, row_bytes, cr0, G.nq, CPT * cw, coff0, sb + TB, lane);
+                if constexpr (CPT == 2) {
+                    copy_rows<D>(qb, row_bytes, cr0, G.nq, 2 * cw + 1, coff1, sb, lane);
+                    copy_rows<D>(db, row_bytes, cr0, G.nq, 2 * cw + 1, coff1, sb + TB, lane);
+                }
                 dma4(ld_lane - l32 + (cli - cr0) + min(cr0 + l32, G.nq - 1), sb + 2 * TB);
             }
         };
@@ -762,7 +836,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                 issue(i);
                 advance();
             }
-            wait_vmcnt<5 * (PDK - 1)>();
+            wait_vmcnt<NCP * (PDK - 1)>();
         }
         lds_barrier();
         int st = NSK - 1, cst = PDK, q0 = row_first;
@@ -826,7 +900,7 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
                     for (int dt = 0; dt < D / 32; ++dt)
                         acc[dt] = MFMA(at[qc][dt], ob[qc], acc[dt], 0, 0, 0);
             }
-            wait_vmcnt<5 * (PDK - 1)>();   // tile it + 1 has landed
+            wait_vmcnt<NCP * (PDK - 1)>();   // tile it + 1 has landed
             lds_barrier();
             st = st + 1 == NSK ? 0 : st + 1;
             if (it > 0) next_row(q0);
@@ -863,11 +937,12 @@ __device__ __forceinline__ void dkdv_item(const BwdParams &p, const KvStep &io, 
 }
 
 // One step's dK/dV.
+template <int D>
 __global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
-    dkdv_item<false>(p, KvStep{p.k, p.v, p.dk, p.dv, p.mode, p.head_splits, p.tab.tile0}, blockIdx.x,
-              lds);
+    __shared__ __attribute__((aligned(1024))) char lds[dkdv_lds<D>()];
+    dkdv_item<false, D>(p, KvStep{p.k, p.v, p.dk, p.dv, p.mode, p.head_splits, p.tab.tile0},
+                        blockIdx.x, lds);
 }
 
 // The dK/dV of several steps of one rank's share in one grid.  Each step
@@ -901,9 +976,10 @@ struct DkdvStepsParams {
 };
 static_assert(sizeof(DkdvStepsParams) <= 4096, "kernel arguments");
 
+template <int D>
 __global__ void __launch_bounds__(64 * NWK) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv_steps(DkdvStepsParams sp) {
-    __shared__ __attribute__((aligned(1024))) char lds[DKDV_LDS];
+    __shared__ __attribute__((aligned(1024))) char lds[dkdv_lds<D>()];
     const int item = blockIdx.x;
     int j = 0;
     while (j + 1 < sp.nruns && sp.run[j + 1].item0 <= item) ++j;
@@ -911,7 +987,7 @@ attn_bwd_dkdv_steps(DkdvStepsParams sp) {
     const KvStepDesc &d = sp.st[rn.step];
     const int inner = sp.p.hkv * sp.p.b;   // workgroups per key tile
     const int w = item - rn.item0;
-    dkdv_item<true>(sp.p,
+    dkdv_item<true, D>(sp.p,
                     KvStep{d.k, d.v, d.dk, d.dv, d.mode, 1,
                            d.mode == CPATTN_KV_FIRST_HALF ? sp.tile0_half : sp.p.tab.tile0},
                     (rn.kt0 + w / inner) * inner + w % inner, lds);
@@ -921,7 +997,7 @@ attn_bwd_dkdv_steps(DkdvStepsParams sp) {
 // D[n, h, i] = sum_t dO[n, i, h, t] O[n, i, h, t]: one thread per (n, i, h).
 // PREP: writes -D, and -L[n, h, i] * inv_scale to nl (the terms the share's
 // backward grids start S and dP from).
-template <bool PREP>
+template <bool PREP, int D>
 __global__ void __launch_bounds__(256) bwd_delta(const float *o, const uint16_t *dout,
                                                  float *delta, int64_t rows, int hq,
                                                  int64_t two_c, const float *lse,
@@ -961,24 +1037,24 @@ __global__ void __launch_bounds__(256) fill_zero(float *x, int64_t n4) {
 
 }  // namespace
 
-hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o, const void *dout,
-                            float *delta, hipStream_t stream) {
+hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, int d, const float *o,
+                            const void *dout, float *delta, hipStream_t stream) {
     const int64_t rows = b * two_c * hq;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_delta<false>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       stream, o, (const uint16_t *)dout, delta, rows, hq, two_c, nullptr, 0.0f,
-                       nullptr);
+    auto *fn = d == 64 ? bwd_delta<false, 64> : bwd_delta<false, 128>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, o,
+                       (const uint16_t *)dout, delta, rows, hq, two_c, nullptr, 0.0f, nullptr);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, const float *o, const void *dout,
-                           const float *lse, float inv_scale, float *nl, float *nd,
-                           hipStream_t stream) {
+hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, int d, const float *o,
+                           const void *dout, const float *lse, float inv_scale, float *nl,
+                           float *nd, hipStream_t stream) {
     const int64_t rows = b * two_c * hq;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_delta<true>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       stream, o, (const uint16_t *)dout, nd, rows, hq, two_c, lse, inv_scale,
-                       nl);
+    auto *fn = d == 64 ? bwd_delta<true, 64> : bwd_delta<true, 128>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, o,
+                       (const uint16_t *)dout, nd, rows, hq, two_c, lse, inv_scale, nl);
     return hipGetLastError();
 }
 
@@ -1037,8 +1113,8 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
                                 float *dv, hipStream_t stream, bool with_dkdv) {
     BwdParams p = make_params(g, tab, mode, q, k, v, dout, lse, delta, dq, dk, dv);
     const int64_t nqt = fill_tiles(p, tab, mode, false);
-    hipLaunchKernelGGL(attn_bwd_dq, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * NWB), 0,
-                       stream, p);
+    auto *dq_fn = g.d == 64 ? attn_bwd_dq<64> : attn_bwd_dq<128>;
+    hipLaunchKernelGGL(dq_fn, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * NWB), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !with_dkdv) return e;
     // the group's heads split so the grid has at least ~2 workgroups per CU
@@ -1048,8 +1124,9 @@ hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode
     while (p.head_splits < p.group && p.group % (p.head_splits * 2) == 0 &&
            base_wgs * p.head_splits < 512)
         p.head_splits *= 2;
-    hipLaunchKernelGGL(attn_bwd_dkdv, dim3((unsigned)(base_wgs * p.head_splits)),
-                       dim3(64 * NWK), 0, stream, p);
+    auto *kv_fn = g.d == 64 ? attn_bwd_dkdv<64> : attn_bwd_dkdv<128>;
+    hipLaunchKernelGGL(kv_fn, dim3((unsigned)(base_wgs * p.head_splits)), dim3(64 * NWK), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -1061,20 +1138,21 @@ hipError_t launch_bwd_dq_share_bf16(const StepGeom &g, const SeqTable &tab, int 
                               nullptr);
     p.rank = rank;
     p.cp = cp;
-    p.block_elems = g.b * g.two_c * g.hkv * D;
+    p.block_elems = g.b * g.two_c * g.hkv * g.d;
     // query tiles of the 2c local rows of every sample: 256-row tiles (8
     // waves) when they still give two workgroups per CU and no sample is
     // packed (short samples would leave half of a tile's waves idle), else
-    // 128-row ones
+    // 128-row ones.  With d = 64 a tile is four copies per tensor, one per
+    // wave of 4: always 128-row tiles.
     const int64_t nqt8 = fill_tiles(p, tab, CPATTN_CAUSAL, false, 8);
-    if (tab.nseq == 1 && nqt8 * g.hq * g.b >= 2 * (int64_t)device_cu_count()) {
-        hipLaunchKernelGGL(attn_bwd_dq_share<8>, dim3((unsigned)(nqt8 * g.hq * g.b)), dim3(64 * 8),
-                           0, stream, p);
+    if (g.d == 128 && tab.nseq == 1 && nqt8 * g.hq * g.b >= 2 * (int64_t)device_cu_count()) {
+        auto *fn8 = attn_bwd_dq_share<8, 128>;
+        hipLaunchKernelGGL(fn8, dim3((unsigned)(nqt8 * g.hq * g.b)), dim3(64 * 8), 0, stream, p);
         return hipGetLastError();
     }
     const int64_t nqt = fill_tiles(p, tab, CPATTN_CAUSAL, false, 4);
-    hipLaunchKernelGGL(attn_bwd_dq_share<4>, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * 4), 0,
-                       stream, p);
+    auto *fn4 = g.d == 64 ? attn_bwd_dq_share<4, 64> : attn_bwd_dq_share<4, 128>;
+    hipLaunchKernelGGL(fn4, dim3((unsigned)(nqt * g.hq * g.b)), dim3(64 * 4), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1153,8 +1231,8 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &
             items += rc[a] * inner;
         }
         sp.nruns = nr;
-        hipLaunchKernelGGL(attn_bwd_dkdv_steps, dim3((unsigned)items), dim3(64 * NWK), 0,
-                           stream, sp);
+        auto *fn = g[0].d == 64 ? attn_bwd_dkdv_steps<64> : attn_bwd_dkdv_steps<128>;
+        hipLaunchKernelGGL(fn, dim3((unsigned)items), dim3(64 * NWK), 0, stream, sp);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -84,7 +84,7 @@ hipError_t launch_fused_bf16(const FusedGeom &f, const void *qz, const void *kz,
                              const void *vz, void *o, bool out_bf16, float *lse,
                              hipStream_t stream);
 
-// Backward of one step (bf16, d = 128) for every packed sample of 'tab' in
+// Backward of one step (bf16, d = 64 or 128) for every packed sample of 'tab' in
 // step mode 'mode': dq += , dk += , dv += (fp32).  g supplies b, two_c (the
 // local rows), the heads and the scale.
 hipError_t launch_step_bwd_bf16(const StepGeom &g, const SeqTable &tab, int mode,
@@ -109,14 +109,15 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &
                                       const float *nl, const float *nd, float *const *dk,
                                       float *const *dv, hipStream_t stream);
 
-// delta[n, h, i] = sum_t dout[n, i, h, t] o[n, i, h, t]; o fp32, dout bf16.
-hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o,
+// delta[n, h, i] = sum_t dout[n, i, h, t] o[n, i, h, t]; o fp32, dout bf16;
+// t < d (64 or 128).
+hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, int d, const float *o,
                             const void *dout, float *delta, hipStream_t stream);
 // The per-row terms the share's backward grids start their sums from:
 // nl[n, h, i] = -lse[n, h, i] * inv_scale and nd[n, h, i] = -delta[n, h, i].
-hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, const float *o, const void *dout,
-                           const float *lse, float inv_scale, float *nl, float *nd,
-                           hipStream_t stream);
+hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, int d, const float *o,
+                           const void *dout, const float *lse, float inv_scale, float *nl,
+                           float *nd, hipStream_t stream);
 
 // Compute units of the current device (cached per device), 0 if it cannot
 // be queried.

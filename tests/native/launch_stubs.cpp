@@ -115,16 +115,18 @@ hipError_t launch_bwd_dkdv_steps_bf16(int n, const StepGeom *g, const SeqTable &
     return hipSuccess;
 }
 
-hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, const float *o, const void *dout,
-                            float *delta, hipStream_t) {
-    REQUIRE(b >= 1 && two_c >= 2 && hq >= 1 && o && dout && delta);
+hipError_t launch_bwd_delta(int64_t b, int64_t two_c, int hq, int d, const float *o,
+                            const void *dout, float *delta, hipStream_t) {
+    REQUIRE(b >= 1 && two_c >= 2 && hq >= 1 && (d == 64 || d == 128) && o && dout && delta);
     ++stubs::launches[stubs::DELTA];
     return hipSuccess;
 }
 
-hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, const float *o, const void *dout,
-                           const float *lse, float inv_scale, float *nl, float *nd, hipStream_t) {
-    REQUIRE(b >= 1 && two_c >= 2 && hq >= 1 && o && dout && lse && nl && nd);
+hipError_t launch_bwd_prep(int64_t b, int64_t two_c, int hq, int d, const float *o,
+                           const void *dout, const float *lse, float inv_scale, float *nl,
+                           float *nd, hipStream_t) {
+    REQUIRE(b >= 1 && two_c >= 2 && hq >= 1 && (d == 64 || d == 128) && o && dout && lse && nl &&
+            nd);
     REQUIRE(inv_scale > 0.0f && nd == nl + b * hq * two_c);
     ++stubs::launches[stubs::DELTA];
     return hipSuccess;

@@ -210,19 +210,19 @@ def test_backward_grids_past_32_bits_rejected():
     assert L.cpattn_bwd_delta(ctypes.byref(d2), ALIGNED, ALIGNED, ALIGNED, 0) == C.CPATTN_ESHAPE
 
 
-def test_backward_refuses_head_dim_64():
-    """The bf16 forward entry points take d = 64 and 128; the backward ones
-    d = 128 only, and say so before any launch."""
+def test_backward_head_dims():
+    """The bf16 backward entry points take d = 64 and 128 (here: validation
+    passes the shape and stops at a NULL pointer) and refuse other d."""
     L = C.lib()
-    d = _dims(b=1, s=4096, hq=8, hkv=2, d=64, cp=4)
-    args = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), 0] + [ALIGNED] * 11 + [0]
-    assert L.cpattn_backward(*args) == C.CPATTN_ESHAPE
-    sargs = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), C.CPATTN_CAUSAL] + \
-        [ALIGNED] * 10 + [0]
-    assert L.cpattn_step_bwd(*sargs) == C.CPATTN_ESHAPE
-    assert L.cpattn_bwd_delta(ctypes.byref(d), ALIGNED, ALIGNED, ALIGNED, 0) == C.CPATTN_ESHAPE
-    # the forward step of the same dims passes validation up to the pointers
-    assert _step(d, dtype=C.CPATTN_BF16, ptrs=[0] + [ALIGNED] * 4) == C.CPATTN_EINVAL
+    for d_ok, want in ((64, C.CPATTN_EINVAL), (96, C.CPATTN_ESHAPE)):
+        d = _dims(b=1, s=4096, hq=8, hkv=2, d=d_ok, cp=4)
+        args = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), 0, None] + \
+            [ALIGNED] * 9 + [0]
+        assert L.cpattn_backward(*args) == want
+        sargs = [ctypes.byref(d), C.CPATTN_BF16, ctypes.c_float(0.0), C.CPATTN_CAUSAL, None] + \
+            [ALIGNED] * 8 + [0]
+        assert L.cpattn_step_bwd(*sargs) == want
+        assert L.cpattn_bwd_delta(ctypes.byref(d), None, ALIGNED, ALIGNED, 0) == want
 
 
 def test_forward_steps_validation():

@@ -66,11 +66,18 @@ ONE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp1",
 # more ranks than one merge pass takes (64), chunks of 3 rows
 FINE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp128",
                               s=2 * 128 * 3, hq=4, hkv=2, cp=128)
-EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP, "cp128": FINE_CP}
+# 64-wide heads: GQA with ragged tiles, MHA with wide logits and b = 2
+D64_GQA = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_d64_cp4",
+                              s=2 * 4 * 100, d=64)
+D64_MHA = dataclasses.replace(WORKLOADS["bf16_mha_s16k_cp4_widelogits"],
+                              name="bf16_mha_d64_cp4_widelogits", s=2 * 4 * 96, d=64)
+EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP, "cp128": FINE_CP, "d64_gqa": D64_GQA,
+         "d64_mha": D64_MHA}
 
 
 @pytest.mark.parametrize("name,s", REDUCED + [("cp40", WIDE_CP.s), ("cp1", ONE_CP.s),
-                                              ("cp128", FINE_CP.s)])
+                                              ("cp128", FINE_CP.s), ("d64_gqa", D64_GQA.s),
+                                              ("d64_mha", D64_MHA.s)])
 def test_backward_all_ranks_reduced(name, s):
     w = EXTRA[name] if name in EXTRA else small(WORKLOADS[name], s)
     say(f"backward reduced {name} s={s}")
@@ -100,10 +107,11 @@ def test_backward_all_ranks_reduced(name, s):
     assert_grad("dV", ocp.unpartition(dv_z, w.s), dv)
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("mode", [C.CPATTN_CAUSAL, C.CPATTN_KV_FIRST_HALF, C.CPATTN_Q_SECOND_HALF])
-def test_step_bwd_each_mode(mode):
-    w = small(WORKLOADS["bf16_gqa_s8k_cp4"], 2 * 4 * 72)
-    say(f"step backward mode {ocp.MODE_NAMES[mode]}")
+def test_step_bwd_each_mode(mode, d):
+    w = dataclasses.replace(small(WORKLOADS["bf16_gqa_s8k_cp4"], 2 * 4 * 72), d=d)
+    say(f"step backward mode {ocp.MODE_NAMES[mode]} d={d}")
     rng = np.random.default_rng(7 + mode)
     two_c, c = 2 * w.c, w.c
     shp_q, shp_k = (w.b, two_c, w.hq, w.d), (w.b, two_c, w.hkv, w.d)
@@ -160,16 +168,18 @@ def test_backward_full_size_sampled_dq():
     assert_grad("dQ rows", g["dq"].cpu().numpy()[:, rows], dq_ref)
 
 
-@pytest.mark.parametrize("name", ["bf16_gqa_s32k_cp8", "bf16_mha_s16k_cp4_widelogits"])
-def test_backward_full_size_equals_step_entry_points(name):
+@pytest.mark.parametrize("name,d", [("bf16_gqa_s32k_cp8", 128),
+                                    ("bf16_mha_s16k_cp4_widelogits", 128),
+                                    ("bf16_gqa_s32k_cp8", 64)])
+def test_backward_full_size_equals_step_entry_points(name, d):
     """At full size every element of the share's gradients (the one-grid dK/dV
     and the dQ grid of 256-row tiles that these sizes select) against the
     same share through cpattn_step_bwd, one zigzag step at a time; that entry
     point is held to the oracle per mode above.  The two differ only in the
     order of the fp32 sums, so the bound is the same relative one."""
-    w = WORKLOADS[name]
+    w = dataclasses.replace(WORKLOADS[name], d=d)
     r = w.rank
-    say(f"backward full {name}: rank {r}, share vs per-step entry points")
+    say(f"backward full {name} d={d}: rank {r}, share vs per-step entry points")
     q, k, v = make_inputs(w)
     P = CPProblem(w, q, k, v)
     P.partition()

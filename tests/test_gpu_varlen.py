@@ -193,12 +193,14 @@ BWD = [("bf16_gqa_s8k_cp4", [100, 1, 37, 64]),
        ("bf16_gqa_s128k_cp16_rope", [24, 7, 9])]
 
 
-@pytest.mark.parametrize("name,chunks", BWD)
-def test_backward_varlen_all_ranks(name, chunks):
-    base = WORKLOADS[name]
+@pytest.mark.parametrize("name,chunks,d", [b + (128,) for b in BWD] +
+                         [("bf16_gqa_s8k_cp4", [100, 1, 37, 64], 64),
+                          ("bf16_gqa_s128k_cp16_rope", [24, 7, 9], 64)])
+def test_backward_varlen_all_ranks(name, chunks, d):
+    base = dataclasses.replace(WORKLOADS[name], d=d)
     cu = _cu(base.cp, chunks)
     w = small(base, int(cu[-1]))
-    say(f"backward varlen {name} cu={cu.tolist()}")
+    say(f"backward varlen {name} cu={cu.tolist()} d={d}")
     q, k, v = make_inputs(w)
     rng = np.random.default_rng(99)
     do = f32_to_bf16_bits(rng.standard_normal((w.b, w.s, w.hq, w.d)).astype(np.float32))

@@ -34,7 +34,9 @@
 // ds_read_b128) and over its rows (8 rows of one column per lane,
 // ds_read_b64_tr_b16).  One XOR swizzle keeps both reads free of bank
 // conflicts: 16-byte chunk c of tile row r sits at chunk c ^ u_swz(r), with
-// u_swz(r) = 4 (r % 4) + (r / 4) % 4.  Tiles are copied global -> LDS
+// u_swz(r) = 4 (r % 4) + (r / 4) % 4 (256-byte rows, d = 128; 128-byte rows,
+// d = 64, use h_swz).  Every kernel is a template over the head dimension
+// d = 64 or 128.  Tiles are copied global -> LDS
 // directly (global_load_lds, no register round trip) several tiles ahead of
 // their use into a ring of stages; each lane copies fixed chunks, chosen so
 // that the copy's linear LDS order is the swizzled layout.  One barrier per
@@ -236,8 +238,9 @@ __device__ __forceinline__ void copy_rows(const uint16_t *base, int64_t row_byte
 // ---------------------------------------------------------------------------
 // dQ: workgroup = NW waves (4 or 8) x 32 query rows of one (batch, head);
 // 32-key tiles of K and V stream through NSQ stages, PDQ tiles ahead.  Wave
-// w copies rows 4w.. (and, with 4 waves, 4(w+4)..) of both tiles.  With 8
-// waves a copied tile serves twice the rows (one workgroup per CU instead of
+// w issues copy w (and, with 4 waves at d = 128, copy w + 4) of both tiles;
+// a copy is 4 rows at d = 128 and 8 at d = 64.  With 8 waves (d = 128 only)
+// a copied tile serves twice the rows (one workgroup per CU instead of
 // two); the share's launcher takes 8 when that still leaves two workgroups
 // per CU.
 constexpr int NWB = 4;                     // waves of the single step's dq

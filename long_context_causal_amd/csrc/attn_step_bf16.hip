@@ -57,8 +57,8 @@
 // LDS (64 banks x 4 bytes on gfx950): rows are 2d bytes (256 for d = 128,
 // 128 for d = 64, one template per head dimension); 16-byte chunks are
 // XOR-swizzled per row (see Kernel::k_swz / v_swz) so every ds_read_b128 /
-// ds_read_b64_tr_b16 phase hits distinct banks.  With d = 64 a phase of
-// matrix steps does four MFMAs on each of four k-steps instead of eight.
+// ds_read_b64_tr_b16 phase hits distinct banks.  With d = 64 a matrix phase
+// has four steps of four MFMAs instead of eight.
 // The global -> LDS copies are issued from inline assembly, so the compiler
 // does not track them (it would otherwise wait for every copy in flight
 // before each LDS read, as it cannot tell the stages apart); explicit vmcnt

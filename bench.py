@@ -331,9 +331,10 @@ def _kernel_source_digest():
     return h.hexdigest()
 
 
-def digest(prof_dir):
+def digest(prof_dir, out_dir=None):
     """The three profiles/ summaries of the headline workload from the csv
-    output of PROFILE_COMMANDS under prof_dir."""
+    output of PROFILE_COMMANDS under prof_dir (written to out_dir, by default
+    the repository's profiles/)."""
     import collections
     import statistics
     from long_context_causal_amd.inputs import HEADLINE, WORKLOADS
@@ -521,10 +522,11 @@ def digest(prof_dir):
                     lines.append(f"   {c.lower()[9:]}_per_mfma: {mean(sq[(k, g, c)]) / mean(mf):.2f}")
     out_files[f"attn_steps_bf16__{w.name}__sq_counters.txt"] = lines
 
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
     for fname, text in out_files.items():
-        with open(os.path.join(ROOT, "profiles", fname), "w") as f:
+        with open(os.path.join(out_dir, fname), "w") as f:
             f.write("\n".join(text) + "\n")
-        print(f"wrote profiles/{fname}")
+        print(f"wrote {os.path.join(out_dir, fname)}")
 
 
 def main():

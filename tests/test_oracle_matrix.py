@@ -13,6 +13,12 @@ keys, a transposed output) fails at least one of them:
 * closed form: Q = 0 and V[j] = j give L[i] = ln(kend_i) and O[i] =
   (kend_i - 1) / 2;
 * the run size: tiny and huge score-matrix bounds give the same result.
+
+The backward form (``attention_rows_bwd_matrix``) is pinned the same way:
+to the C core's row-at-a-time backward (itself pinned by central finite
+differences), to torch autograd through fp64 scaled_dot_product_attention,
+to the closed form of dV when Q = 0 (uniform weights: dV[j] sums dO[i] /
+kend[i] over the rows that see key j), and to its own run size.
 """
 import math
 
@@ -20,8 +26,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_rows, causal_attention
-from oracle.matrix import attention_at_positions, attention_rows_matrix
+from oracle import attention_rows, attention_rows_bwd, causal_attention
+from oracle.matrix import attention_at_positions, attention_rows_bwd_matrix, attention_rows_matrix
 
 
 @pytest.mark.parametrize("b,nq,nk,hq,hkv,d", [(1, 1, 1, 1, 1, 8), (2, 37, 50, 4, 2, 16),
@@ -91,3 +97,64 @@ def test_explicit_scale():
     np.testing.assert_allclose(o, o_ref, atol=1e-12)
     np.testing.assert_allclose(l, l_ref, atol=1e-12)
     assert not math.isclose(0.3, 1 / math.sqrt(8))
+
+
+@pytest.mark.parametrize("b,nq,nk,hq,hkv,d", [(1, 1, 1, 1, 1, 8), (2, 37, 50, 4, 2, 16),
+                                              (3, 20, 33, 6, 3, 4)])
+def test_bwd_matches_c_core_ragged(b, nq, nk, hq, hkv, d):
+    rng = np.random.default_rng(nq * 7 + nk)
+    q = rng.standard_normal((b, nq, hq, d))
+    k = rng.standard_normal((b, nk, hkv, d)) * 2
+    v = rng.standard_normal((b, nk, hkv, d))
+    do = rng.standard_normal((b, nq, hq, d))
+    kend = rng.integers(0, nk + 1, size=nq)
+    kend[0] = 0                                # a row that sees no key
+    kend[-1] = nk
+    got = attention_rows_bwd_matrix(q, k, v, do, kend, max_elems=97)
+    ref = attention_rows_bwd(q, k, v, do, kend)
+    for x, y in zip(got, ref):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+    assert np.all(got[0][:, kend == 0] == 0.0)
+
+
+@pytest.mark.parametrize("b,s,hq,hkv,d", [(1, 45, 4, 4, 16), (2, 64, 8, 2, 32)])
+def test_bwd_matches_torch_autograd_causal(b, s, hq, hkv, d):
+    rng = np.random.default_rng(s + 1)
+    q, do = (rng.standard_normal((b, s, hq, d)) for _ in range(2))
+    k, v = (rng.standard_normal((b, s, hkv, d)) for _ in range(2))
+    dq, dk, dv = attention_rows_bwd_matrix(q, k, v, do, np.arange(1, s + 1), max_elems=700)
+    g = hq // hkv
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3).clone().requires_grad_(True)
+                  for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1), is_causal=True)
+    o.backward(torch.from_numpy(do).permute(0, 2, 1, 3))
+    for got, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(got, t.grad.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-11)
+
+
+def test_bwd_zero_queries_closed_form_dv():
+    rng = np.random.default_rng(3)
+    nq, nk, hq, d = 30, 41, 4, 8
+    q = np.zeros((1, nq, hq, d))
+    k, v = (rng.standard_normal((1, nk, 2, d)) for _ in range(2))
+    do = rng.standard_normal((1, nq, hq, d))
+    kend = rng.integers(1, nk + 1, size=nq)
+    _, _, dv = attention_rows_bwd_matrix(q, k, v, do, kend, max_elems=50)
+    ref = np.zeros((1, nk, 2, d))
+    for i in range(nq):
+        for h in range(hq):
+            ref[0, :kend[i], h // 2, :] += do[0, i, h, :] / kend[i]
+    np.testing.assert_allclose(dv, ref, rtol=0, atol=1e-12)
+
+
+def test_bwd_run_size_does_not_matter():
+    rng = np.random.default_rng(9)
+    s, hq, hkv, d = 80, 4, 2, 16
+    q, do = (rng.standard_normal((2, s, hq, d)) for _ in range(2))
+    k, v = (rng.standard_normal((2, s, hkv, d)) for _ in range(2))
+    kend = np.arange(1, s + 1)
+    a = attention_rows_bwd_matrix(q, k, v, do, kend, max_elems=1)
+    b = attention_rows_bwd_matrix(q, k, v, do, kend, max_elems=1 << 30)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)

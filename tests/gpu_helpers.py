@@ -13,6 +13,10 @@ from oracle import cp as ocp
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 2e-3
 F32_MAX_ABS = 1e-5
+# backward bound (bf16 rounding of P and dS in the products, 2^-9 relative
+# per term; gradients are sums with cancellation, so the error is measured
+# against the gradient's own scale), per gradient
+GRAD_MAX_REL, GRAD_MEAN_REL = 1e-2, 5e-3
 
 
 def say(msg):
@@ -39,6 +43,26 @@ def assert_close(name, got, want, max_abs, mean_abs=None):
     assert mx <= max_abs, f"{name}: max abs {mx} > {max_abs}"
     if mean_abs is not None:
         assert mn <= mean_abs, f"{name}: mean abs {mn} > {mean_abs}"
+
+
+def assert_grad(name, got, ref):
+    """max |err| <= GRAD_MAX_REL max |ref| and mean |err| <= GRAD_MEAN_REL
+    mean |ref|."""
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    mx, mn = err.max(), err.mean()
+    rmx, rmn = np.abs(ref).max(), np.abs(ref).mean()
+    say(f"  [{name}] max_err={mx:.3e} ({mx / rmx:.2e} of max|ref|) "
+        f"mean_err={mn:.3e} ({mn / rmn:.2e} of mean|ref|)")
+    assert mx <= GRAD_MAX_REL * rmx, f"{name}: max error {mx} > {GRAD_MAX_REL} * {rmx}"
+    assert mn <= GRAD_MEAN_REL * rmn, f"{name}: mean error {mn} > {GRAD_MEAN_REL} * {rmn}"
+
+
+def seeded_dout(w: Workload, seed=99):
+    """dO of a workload: seeded standard normal, rounded to bf16 bits."""
+    from long_context_causal_amd.inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.standard_normal((w.b, w.s, w.hq, w.d)).astype(np.float32))
 
 
 def small(w: Workload, s: int, b=None) -> Workload:

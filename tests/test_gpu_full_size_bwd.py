@@ -1,0 +1,92 @@
+"""GPU backward parity at the full sizes of the bf16 workloads, over every
+element.
+
+Each rank runs its forward share (the cp steps' grid, then the merge) and
+its backward share (cpattn_backward) with a seeded bf16 dO, as in
+training: the rank's own merged O and L feed its backward.  The ranks'
+dK/dV contributions are summed per owner (what the reduce-scatter does,
+"超大规模集群下大语言模型训练实操指南", the backward's all-gather and
+reduce-scatter of K/V) and every rank's dQ is put back in sequence order.
+Both are compared with the gradients of the non-CP causal attention from
+the oracle's matrix form (oracle/matrix.py) on the same bf16 bits widened
+to fp64:
+
+* 8k GQA cp=4 and 16k MHA b=2 cp=4 (wide logits): dQ, dK and dV, every
+  element;
+* 32k GQA cp=8: dQ of the measured rank (rank 3), all 4096 of its rows
+  and every head (its dK/dV contributions are checked against the
+  per-step entry point in test_gpu_backward.py).
+
+Bound, per gradient: max |err| <= 1e-2 max |ref| and mean |err| <= 5e-3
+mean |ref| (bf16 rounding of P and dS in the products).
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import (C, CPProblem, as_f32, assert_grad, make_inputs, ocp, say, seeded_dout,
+                         to_device, torch)
+from long_context_causal_amd.inputs import WORKLOADS, f32_to_bf16_bits
+from oracle.matrix import attention_rows_bwd_matrix
+
+pytestmark = pytest.mark.gpu
+
+
+def _rank_backward(P, w, r, doz_r):
+    """(dQ [b, 2c, hq, d], dK/dV contributions [cp, b, 2c, hkv, d]) of rank r."""
+    buf = P.alloc_rank(r, C.CPATTN_F32)
+    P.forward(buf)
+    g = P.alloc_grads(r)
+    P.backward(g, buf["o"], buf["lse"], to_device(f32_to_bf16_bits(doz_r.astype(np.float32))))
+    torch.cuda.synchronize()
+    out = tuple(g[x].cpu().numpy() for x in ("dq", "dkz", "dvz"))
+    del buf, g
+    return out
+
+
+@pytest.mark.parametrize("name", ["bf16_gqa_s8k_cp4", "bf16_mha_s16k_cp4_widelogits"])
+def test_backward_full_size_every_element(name):
+    w = WORKLOADS[name]
+    say(f"backward full {name}: every rank, every element")
+    q, k, v = make_inputs(w)
+    do = seeded_dout(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    doz = ocp.partition(as_f32(do), w.cp)
+    two_c = 2 * w.c
+    dq_z = np.zeros((w.cp, w.b, two_c, w.hq, w.d), np.float32)
+    dk_z = np.zeros((w.cp, w.b, two_c, w.hkv, w.d), np.float64)
+    dv_z = np.zeros_like(dk_z)
+    for r in range(w.cp):
+        say(f"  rank {r}: gpu forward and backward")
+        dq_z[r], dk_r, dv_r = _rank_backward(P, w, r, doz[r])
+        dk_z += dk_r
+        dv_z += dv_r
+    del P
+    torch.cuda.empty_cache()
+    say("  oracle: causal attention backward, matrix form")
+    f64 = lambda x: as_f32(x).astype(np.float64)
+    dq, dk, dv = attention_rows_bwd_matrix(f64(q), f64(k), f64(v), f64(do), np.arange(1, w.s + 1),
+                                          max_elems=1 << 24)
+    assert_grad("dQ", ocp.unpartition(dq_z, w.s).astype(np.float64), dq)
+    assert_grad("dK", ocp.unpartition(dk_z, w.s), dk)
+    assert_grad("dV", ocp.unpartition(dv_z, w.s), dv)
+
+
+def test_backward_full_size_headline_rank_dq():
+    w = WORKLOADS["bf16_gqa_s32k_cp8"]
+    r = w.rank
+    say(f"backward full {w.name}: rank {r} dQ, every row")
+    q, k, v = make_inputs(w)
+    do = seeded_dout(w)
+    P = CPProblem(w, q, k, v)
+    P.partition()
+    dq_r, _, _ = _rank_backward(P, w, r, ocp.partition(as_f32(do), w.cp)[r])
+    del P
+    torch.cuda.empty_cache()
+    pos = ocp.zigzag_positions(w.s, w.cp, r)
+    hi = int(pos.max()) + 1
+    f64 = lambda x: as_f32(x).astype(np.float64)
+    say(f"  oracle: {len(pos)} rows against up to {hi} keys, matrix form")
+    dq, _, _ = attention_rows_bwd_matrix(f64(q[:, pos]), f64(k[:, :hi]), f64(v[:, :hi]),
+                                         f64(do[:, pos]), pos + 1, max_elems=1 << 24)
+    assert_grad("dQ", dq_r.astype(np.float64), dq)

@@ -174,17 +174,7 @@ def test_fused_varlen_full_size_sampled_rows():
 from long_context_causal_amd.inputs import f32_to_bf16_bits  # noqa: E402
 from long_context_causal_amd.runner import to_device  # noqa: E402
 
-GRAD_MAX_REL, GRAD_MEAN_REL = 1e-2, 5e-3      # as the unpacked backward (test_gpu_backward)
-
-
-def _assert_grad(name, got, ref):
-    err = np.abs(got - ref)
-    assert np.all(np.isfinite(got)), f"{name}: non-finite"
-    mx, mn = err.max(), err.mean()
-    rmx, rmn = np.abs(ref).max(), np.abs(ref).mean()
-    say(f"  [{name}] max_err={mx:.3e} ({mx / rmx:.2e} of max|ref|) "
-        f"mean_err={mn:.3e} ({mn / rmn:.2e} of mean|ref|)")
-    assert mx <= GRAD_MAX_REL * rmx and mn <= GRAD_MEAN_REL * rmn
+from gpu_helpers import assert_grad as _assert_grad  # noqa: E402  (the unpacked backward's bound)
 
 
 BWD = [("bf16_gqa_s8k_cp4", [100, 1, 37, 64]),

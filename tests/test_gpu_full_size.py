@@ -11,10 +11,14 @@ causal attention (oracle/matrix.py) on the same bf16 bits widened to fp64:
 * 32k GQA cp=8: every rank, every row;
 * 128k GQA cp=16 with RoPE at global positions: the measured rank 7, all
   its 8192 rows, in four blocks of 2048 local rows (one test each, so no
-  test runs for long without output).
+  test runs for long without output);
+* 64-wide heads (the same inputs drawn at d = 64): every rank of the 8k GQA
+  dims and the measured rank of the 32k dims, every row.
 
 Bounds: O max abs 2e-2, mean abs 2e-3; L max abs 1e-3.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -26,27 +30,29 @@ from oracle.matrix import attention_at_positions
 pytestmark = pytest.mark.gpu
 
 ROPE_BLOCK = 2048
-CASES = ([("bf16_gqa_s8k_cp4", r, None) for r in range(4)] +
-         [("bf16_mha_s16k_cp4_widelogits", r, None) for r in range(4)] +
-         [("bf16_gqa_s32k_cp8", r, None) for r in range(8)] +
-         [("bf16_gqa_s128k_cp16_rope", 7, blk) for blk in range(4)])
+CASES = ([("bf16_gqa_s8k_cp4", r, None, 128) for r in range(4)] +
+         [("bf16_mha_s16k_cp4_widelogits", r, None, 128) for r in range(4)] +
+         [("bf16_gqa_s32k_cp8", r, None, 128) for r in range(8)] +
+         [("bf16_gqa_s128k_cp16_rope", 7, blk, 128) for blk in range(4)] +
+         [("bf16_gqa_s8k_cp4", r, None, 64) for r in range(4)] +
+         [("bf16_gqa_s32k_cp8", 3, None, 64)])
 
 _state = {}
 
 
-def _workload(name):
+def _workload(name, d=128):
     """Inputs, their fp32 values and the partitioned device problem of one
-    workload, kept while consecutive tests use it."""
-    if _state.get("name") != name:
+    workload (at head dimension d), kept while consecutive tests use it."""
+    if _state.get("key") != (name, d):
         _state.clear()
         torch.cuda.empty_cache()
-        w = WORKLOADS[name]
-        say(f"{name}: inputs and split")
+        w = dataclasses.replace(WORKLOADS[name], d=d)
+        say(f"{name} d={d}: inputs and split")
         q, k, v = make_inputs(w)
         P = CPProblem(w, q, k, v)
         P.partition()
         torch.cuda.synchronize()
-        _state.update(name=name, w=w, P=P, qf=as_f32(q), kf=as_f32(k), vf=as_f32(v), out={})
+        _state.update(key=(name, d), w=w, P=P, qf=as_f32(q), kf=as_f32(k), vf=as_f32(v), out={})
     return _state
 
 
@@ -81,9 +87,9 @@ def _oracle(st, pos):
     return attention_at_positions(qr, kr, st["vf"][:, :hi], pos)
 
 
-@pytest.mark.parametrize("name,rank,block", CASES)
-def test_forward_full_size_every_row(name, rank, block):
-    st = _workload(name)
+@pytest.mark.parametrize("name,rank,block,d", CASES)
+def test_forward_full_size_every_row(name, rank, block, d):
+    st = _workload(name, d)
     w = st["w"]
     o_s, l_s, o_f, l_f = _gpu_outputs(st, rank)
     rows = np.arange(2 * w.c)

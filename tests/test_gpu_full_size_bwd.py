@@ -12,7 +12,7 @@ the oracle's matrix form (oracle/matrix.py) on the same bf16 bits widened
 to fp64:
 
 * 8k GQA cp=4 and 16k MHA b=2 cp=4 (wide logits): dQ, dK and dV, every
-  element;
+  element; the 8k dims also with 64-wide heads;
 * 32k GQA cp=8: dQ of the measured rank (rank 3), all 4096 of its rows
   and every head (its dK/dV contributions are checked against the
   per-step entry point in test_gpu_backward.py).
@@ -20,6 +20,8 @@ to fp64:
 Bound, per gradient: max |err| <= 1e-2 max |ref| and mean |err| <= 5e-3
 mean |ref| (bf16 rounding of P and dS in the products).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -43,10 +45,12 @@ def _rank_backward(P, w, r, doz_r):
     return out
 
 
-@pytest.mark.parametrize("name", ["bf16_gqa_s8k_cp4", "bf16_mha_s16k_cp4_widelogits"])
-def test_backward_full_size_every_element(name):
-    w = WORKLOADS[name]
-    say(f"backward full {name}: every rank, every element")
+@pytest.mark.parametrize("name,d", [("bf16_gqa_s8k_cp4", 128),
+                                    ("bf16_mha_s16k_cp4_widelogits", 128),
+                                    ("bf16_gqa_s8k_cp4", 64)])
+def test_backward_full_size_every_element(name, d):
+    w = dataclasses.replace(WORKLOADS[name], d=d)
+    say(f"backward full {name} d={d}: every rank, every element")
     q, k, v = make_inputs(w)
     do = seeded_dout(w)
     P = CPProblem(w, q, k, v)

@@ -1,6 +1,6 @@
 /*
- * cpattn - context-parallel blockwise causal attention, forward, on one
- * AMD Instinct MI355X (gfx950).
+ * cpattn - context-parallel blockwise causal attention, forward and
+ * backward, on one AMD Instinct MI355X (gfx950).
  *
  * The method ("Megatron-LM 篇", Context Parallel, sections 3.1-3.5; with
  * "超大规模集群下大语言模型训练实操指南", section "CP 与其他技术结合"):
@@ -24,7 +24,8 @@
  * L is the natural-log log-sum-exp of the scaled scores of a row.
  *
  * Ownership: the caller allocates and frees every device buffer; the
- * library allocates no device memory and keeps no state between calls.
+ * library allocates no device memory and keeps no state between calls
+ * (except the scratch array of cpattn_forward_noalloc, described there).
  * Device pointers must be 16-byte aligned and must not overlap unless a
  * function says otherwise.
  *

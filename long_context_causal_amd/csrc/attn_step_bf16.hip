@@ -58,7 +58,10 @@
 // 128 for d = 64, one template per head dimension); 16-byte chunks are
 // XOR-swizzled per row (see Kernel::k_swz / v_swz) so every ds_read_b128 /
 // ds_read_b64_tr_b16 phase hits distinct banks.  With d = 64 a matrix phase
-// has four steps of four MFMAs instead of eight.
+// has four steps of four MFMAs instead of eight; it is then the shorter
+// half of the ping-pong, so the tile's row max and the step of the LDS
+// addresses to the next stages run at its end rather than in the vector
+// half (the same instructions on the same values).
 // The global -> LDS copies are issued from inline assembly, so the compiler
 // does not track them (it would otherwise wait for every copy in flight
 // before each LDS read, as it cannot tell the stages apart); explicit vmcnt
@@ -423,17 +426,24 @@ struct Kernel {
 
     // Vector phase: online softmax of S(t) into P(t), rescaling O and l
     // first when the running max moves by more than the slack.
-    __device__ __forceinline__ static void softmax_phase(const Params &p, State &S,
-                                                         const TileRef &tr, int wrow0,
-                                                         int lane) {
+    // The tile's row max in log2 units (masking the invisible scores first
+    // on tiles that need it).
+    __device__ __forceinline__ static float scaled_tile_max(const Params &p, State &S,
+                                                            const TileRef &tr, int wrow0,
+                                                            int lane) {
         const int hi = lane >> 5;
         const int qrow = wrow0 + (lane & 31);
         // scalar: only tiles crossing the diagonal or the segment end, and
         // waves that straddle a segment's first row, mask
         const bool mask = (tr.key0 + BN > tr.nk) || (tr.causal && tr.key0 + BN - 1 > wrow0) ||
                           wrow0 < tr.min_row;
-        float tmax = mask ? tile_max<true>(tr, S, qrow, hi) : tile_max<false>(tr, S, qrow, hi);
-        tmax = halves_max(tmax) * p.scale_log2;
+        const float tmax =
+            mask ? tile_max<true>(tr, S, qrow, hi) : tile_max<false>(tr, S, qrow, hi);
+        return halves_max(tmax) * p.scale_log2;
+    }
+
+    __device__ __forceinline__ static void softmax_phase(const Params &p, State &S,
+                                                         float tmax) {
         const float m_new = fmaxf(S.m_run, tmax);
         if (__builtin_amdgcn_ballot_w64(m_new > S.m_run + RESCALE_SLACK)) {
             // a row that has seen no visible key yet (m = -inf) keeps alpha 1
@@ -598,32 +608,48 @@ struct Kernel {
         Ahead A;
         read_ahead(S, A);
         if (grp == 1) sync(P, S, 1, lds_addr, wave, cpy);
+        // With 64-wide heads the matrix phase is the shorter half (half the
+        // MFMAs of d = 128 for the same softmax), so the tile max and the
+        // step to the next stages run at its end instead of in the vector
+        // half; the two halves of a SIMD's ping-pong then take about as long
+        // as each other.  The same instructions run in the same order on the
+        // same values either way.
+        constexpr bool EARLY = D == 64;
+        auto advance = [&](int t) {
+            // next tile: the K stage moves from t % NS to (t+1) % NS and the V
+            // stage from (t-1) % NS to t % NS
+            const unsigned kstep = ((t + 1) % NS == 0) ? (unsigned)(-(NS - 1) * 2 * TILEB)
+                                                       : (unsigned)(2 * TILEB);
+            const unsigned vstep = (t % NS == 0) ? (unsigned)(-(NS - 1) * 2 * TILEB)
+                                                 : (unsigned)(2 * TILEB);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) S.koff[kk] += kstep;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) S.voff[dt] += vstep;
+        };
         for (int t = 0; t <= ntiles; ++t) {
             const int hg = 2 * t + grp;    // the barrier this wave last passed
             if (P.comp(t, wrow0) || P.comp(t - 1, wrow0))
                 matrix_phase(S, A);
             if (t == ntiles) break;
-            sync(P, S, hg + 1, lds_addr, wave, cpy);
             if (t > 0) cur = P.next(cur, t);
-            if (P.comp(t, wrow0)) {
-                softmax_phase(p, S, cur, wrow0, lane);
+            const bool comp = P.comp(t, wrow0);
+            float tmax = 0.0f;
+            if constexpr (EARLY) {
+                if (comp) tmax = scaled_tile_max(p, S, cur, wrow0, lane);
+                advance(t);
+            }
+            sync(P, S, hg + 1, lds_addr, wave, cpy);
+            if (comp) {
+                if constexpr (!EARLY) tmax = scaled_tile_max(p, S, cur, wrow0, lane);
+                softmax_phase(p, S, tmax);
             } else {
 #pragma unroll
                 for (int kc = 0; kc < BN / 16; ++kc)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) S.pf[kc][e] = (__bf16)0.0f;
             }
-            {   // next tile, in the vector half: the K stage moves from t % NS to
-                // (t+1) % NS and the V stage from (t-1) % NS to t % NS
-                const unsigned kstep = ((t + 1) % NS == 0) ? (unsigned)(-(NS - 1) * 2 * TILEB)
-                                                           : (unsigned)(2 * TILEB);
-                const unsigned vstep = (t % NS == 0) ? (unsigned)(-(NS - 1) * 2 * TILEB)
-                                                     : (unsigned)(2 * TILEB);
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) S.koff[kk] += kstep;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt) S.voff[dt] += vstep;
-            }
+            if constexpr (!EARLY) advance(t);
             // K(t+1) is resident since barrier 2t+1, V(t) since barrier 2t
             read_ahead(S, A);
             sync(P, S, hg + 2, lds_addr, wave, cpy);

@@ -22,7 +22,11 @@ WIDE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp40
 # one rank: the share is the causal step alone (c = 200, ragged)
 ONE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp1", s=400, hq=4,
                              hkv=2, cp=1)
-EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP}
+# chunks of one row (c = 1): every rank holds two rows, positions r and
+# 2cp - 1 - r; most of its steps see a single key or a single query row
+ONE_ROW = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_c1_cp24", s=2 * 24,
+                              hq=4, hkv=2, cp=24)
+EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP, "c1": ONE_ROW}
 
 # 64-wide heads (the pages fix no head dimension): GQA, MHA with wide
 # logits, RoPE at global positions; ragged chunks
@@ -68,8 +72,9 @@ def test_forward_reduced_all_ranks(name, s, b):
 
 @pytest.mark.parametrize("name", sorted(EXTRA))
 def test_forward_extreme_cp_all_ranks(name):
-    """cp = 40 (more steps than one grid launch takes, ragged chunks c = 40)
-    and cp = 1 (the causal step alone)."""
+    """cp = 40 (more steps than one grid launch takes, ragged chunks c = 40),
+    cp = 1 (the causal step alone) and chunks of one row (c = 1, cp = 24),
+    through cpattn_forward and cpattn_forward_fused."""
     w = EXTRA[name]
     say(f"forward cp={w.cp} s={w.s}")
     q, k, v = make_inputs(w)
@@ -81,6 +86,12 @@ def test_forward_extreme_cp_all_ranks(name):
         pos = ocp.zigzag_positions(w.s, w.cp, r)
         assert_close(f"rank {r} O", o, o_full[:, pos], BF16_MAX_ABS, BF16_MEAN_ABS)
         assert_close(f"rank {r} L", l, l_full[:, :, pos], 1e-3)
+        out = P.alloc_out(r, C.CPATTN_F32)
+        P.forward_fused(out)
+        torch.cuda.synchronize()
+        assert_close(f"rank {r} fused O", out["o"].cpu().numpy(), o_full[:, pos], BF16_MAX_ABS,
+                     BF16_MEAN_ABS)
+        assert_close(f"rank {r} fused L", out["lse"].cpu().numpy(), l_full[:, :, pos], 1e-3)
 
 
 @pytest.mark.parametrize("name", sorted(HEAD64))

@@ -60,13 +60,17 @@ D64_MHA = dataclasses.replace(WORKLOADS["bf16_mha_s16k_cp4_widelogits"],
 # chunks of one row (c = 1): two rows per rank
 ONE_ROW = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_c1_cp24", s=2 * 24,
                               hq=4, hkv=2, cp=24)
+# one query head and one KV head, two batch elements
+ONE_HEAD = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_h1_b2_cp4", s=2 * 4 * 50,
+                               b=2, hq=1, hkv=1)
 EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP, "cp128": FINE_CP, "d64_gqa": D64_GQA,
-         "d64_mha": D64_MHA, "c1": ONE_ROW}
+         "d64_mha": D64_MHA, "c1": ONE_ROW, "h1": ONE_HEAD}
 
 
 @pytest.mark.parametrize("name,s", REDUCED + [("cp40", WIDE_CP.s), ("cp1", ONE_CP.s),
                                               ("cp128", FINE_CP.s), ("d64_gqa", D64_GQA.s),
-                                              ("d64_mha", D64_MHA.s), ("c1", ONE_ROW.s)])
+                                              ("d64_mha", D64_MHA.s), ("c1", ONE_ROW.s),
+                                              ("h1", ONE_HEAD.s)])
 def test_backward_all_ranks_reduced(name, s):
     w = EXTRA[name] if name in EXTRA else small(WORKLOADS[name], s)
     say(f"backward reduced {name} s={s}")

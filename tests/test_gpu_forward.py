@@ -26,7 +26,10 @@ ONE_CP = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_cp1",
 # 2cp - 1 - r; most of its steps see a single key or a single query row
 ONE_ROW = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_gqa_c1_cp24", s=2 * 24,
                               hq=4, hkv=2, cp=24)
-EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP, "c1": ONE_ROW}
+# one query head and one KV head, two batch elements, ragged chunks
+ONE_HEAD = dataclasses.replace(WORKLOADS["bf16_gqa_s8k_cp4"], name="bf16_h1_b2_cp4", s=2 * 4 * 50,
+                               b=2, hq=1, hkv=1)
+EXTRA = {"cp40": WIDE_CP, "cp1": ONE_CP, "c1": ONE_ROW, "h1": ONE_HEAD}
 
 # 64-wide heads (the pages fix no head dimension): GQA, MHA with wide
 # logits, RoPE at global positions; ragged chunks
@@ -73,8 +76,9 @@ def test_forward_reduced_all_ranks(name, s, b):
 @pytest.mark.parametrize("name", sorted(EXTRA))
 def test_forward_extreme_cp_all_ranks(name):
     """cp = 40 (more steps than one grid launch takes, ragged chunks c = 40),
-    cp = 1 (the causal step alone) and chunks of one row (c = 1, cp = 24),
-    through cpattn_forward and cpattn_forward_fused."""
+    cp = 1 (the causal step alone), chunks of one row (c = 1, cp = 24) and a
+    single head (hq = hkv = 1, b = 2), through cpattn_forward and
+    cpattn_forward_fused."""
     w = EXTRA[name]
     say(f"forward cp={w.cp} s={w.s}")
     q, k, v = make_inputs(w)

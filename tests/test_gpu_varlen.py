@@ -245,3 +245,54 @@ def test_backward_varlen_one_sample_is_unpacked():
     # call, bit for bit
     for key in ("dq", "dkz", "dvz"):
         assert torch.equal(g[key], gv[key]), key
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_varlen_most_samples_all_ranks(rope):
+    """The largest packing the ABI takes (CPATTN_MAX_SEQS samples, chunks of
+    1 to 3 rows): every rank's fused forward and backward vs the oracle.
+    With this many samples the backward's run table falls back to one run
+    per step.  With RoPE the split stores the rotated Q and K in bf16, and
+    a row of these short samples sees so few keys that the rounding of its
+    scores shows in L (up to ~1.2e-3), so the reference takes the oracle's
+    rotation rounded to bf16 as its Q and K: the inputs the attention
+    actually gets."""
+    base = WORKLOADS["bf16_gqa_s128k_cp16_rope" if rope else "bf16_gqa_s8k_cp4"]
+    cp = 2
+    cu = _cu(cp, [1 + i % 3 for i in range(C.CPATTN_MAX_SEQS)])
+    w = small(dataclasses.replace(base, cp=cp, hq=4, hkv=2), int(cu[-1]))
+    say(f"varlen {len(cu) - 1} samples, s={w.s}, cp={cp}")
+    q, k, v = make_inputs(w)
+    qf, kf, vf = (as_f32(x).astype(np.float64) for x in (q, k, v))
+    if rope:
+        pos = ovl.sample_positions(cu)
+        qf, kf = (as_f32(f32_to_bf16_bits(ocp.rope(x, pos, w.rope_theta).astype(np.float32)))
+                  .astype(np.float64) for x in (qf, kf))
+    o_ref, l_ref = ovl.packed_causal_attention(qf, kf, vf, cu)
+    rng = np.random.default_rng(11)
+    do = f32_to_bf16_bits(rng.standard_normal((w.b, w.s, w.hq, w.d)).astype(np.float32))
+    P = CPProblem(w, q, k, v, cu_seqlens=cu)
+    P.partition()
+    doz = ovl.partition(as_f32(do), cu, cp)
+    tloc = w.s // cp
+    dq_z = np.zeros((cp, w.b, tloc, w.hq, w.d))
+    dk_z = np.zeros((cp, w.b, tloc, w.hkv, w.d))
+    dv_z = np.zeros_like(dk_z)
+    for r in range(cp):
+        out = P.alloc_out(r, C.CPATTN_F32)
+        P.forward_fused(out)
+        g = P.alloc_grads(r)
+        P.backward(g, out["o"], out["lse"],
+                   to_device(f32_to_bf16_bits(doz[r].astype(np.float32))))
+        torch.cuda.synchronize()
+        rows = ovl.local_rows(cu, cp, r)
+        assert_close(f"rank {r} O", out["o"].cpu().numpy(), o_ref[:, rows], BF16_MAX_ABS,
+                     BF16_MEAN_ABS)
+        assert_close(f"rank {r} L", out["lse"].cpu().numpy(), l_ref[:, :, rows], 1e-3)
+        dq_z[r] = g["dq"].cpu().numpy()
+        dk_z += g["dkz"].cpu().numpy()
+        dv_z += g["dvz"].cpu().numpy()
+    dq, dk, dv = ovl.packed_causal_attention_bwd(qf, kf, vf, as_f32(do).astype(np.float64), cu)
+    _assert_grad("dQ", ovl.unpartition(dq_z, cu), dq)
+    _assert_grad("dK", ovl.unpartition(dk_z, cu), dk)
+    _assert_grad("dV", ovl.unpartition(dv_z, cu), dv)

@@ -70,3 +70,28 @@ def test_backward_entry_point_replays():
     g = P.alloc_grads(r)
     _replays_match(lambda: P.backward(g, buf["o"], buf["lse"], do_r),
                    [g["dq"], g["dkz"], g["dvz"]], "cpattn_backward")
+
+
+def test_split_and_packed_entry_points_replay():
+    """The split (with RoPE at global positions), and the packed-sample
+    split, fused forward and backward: the sample table is copied into the
+    kernel arguments during the call, so the captured launches need no host
+    memory at replay."""
+    import numpy as np
+    w = small(WORKLOADS["bf16_gqa_s128k_cp16_rope"], 2 * 16 * 24)
+    q, k, v = make_inputs(w)
+    P = CPProblem(w, q, k, v)
+    _replays_match(lambda: P.partition(), [P.qz, P.kz, P.vz], "cpattn_partition (RoPE)")
+    cu = np.array([0, 2 * 16 * 5, 2 * 16 * 6, w.s], dtype=np.int64)
+    Pv = CPProblem(w, q, k, v, cu_seqlens=cu)
+    _replays_match(lambda: Pv.partition(), [Pv.qz, Pv.kz, Pv.vz], "cpattn_partition_varlen")
+    r = w.rank
+    out = Pv.alloc_out(r, C.CPATTN_F32)
+    _replays_match(lambda: Pv.forward_fused(out), [out["o"], out["lse"]],
+                   "cpattn_forward_fused_varlen")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6)
+    do_r = torch.randn(out["o"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    g = Pv.alloc_grads(r)
+    _replays_match(lambda: Pv.backward(g, out["o"], out["lse"], do_r),
+                   [g["dq"], g["dkz"], g["dvz"]], "cpattn_backward_varlen")

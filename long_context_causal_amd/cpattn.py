@@ -103,6 +103,7 @@ def lib():
         L.cpattn_backward.argtypes = [D, I, ctypes.c_float, I, P, P, P, P, P, P, P, P, P, P, P]
         L.cpattn_probe_mfma.argtypes = [P, P, I, I, P]
         L.cpattn_device_info.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I)]
+        L.cpattn_probe_fill_lds.argtypes = [ctypes.c_uint, I, P]
         L.cpattn_status_str.argtypes = [I]
         L.cpattn_status_str.restype = ctypes.c_char_p
         for name in ("cpattn_step_mode", "cpattn_partition_positions", "cpattn_partition",
@@ -111,7 +112,8 @@ def lib():
                      "cpattn_forward_fused", "cpattn_forward_noalloc", "cpattn_bwd_delta", "cpattn_step_bwd",
                      "cpattn_backward", "cpattn_partition_positions_varlen",
                      "cpattn_partition_varlen", "cpattn_forward_fused_varlen",
-                     "cpattn_backward_varlen", "cpattn_probe_mfma", "cpattn_device_info"):
+                     "cpattn_backward_varlen", "cpattn_probe_mfma", "cpattn_device_info",
+                     "cpattn_probe_fill_lds"):
             getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -309,3 +311,11 @@ def cpattn_device_info():
     if lib().cpattn_device_info(ctypes.byref(cus), ctypes.byref(khz)) != 0:
         raise RuntimeError("cpattn_device_info failed")
     return cus.value, khz.value
+
+
+def cpattn_probe_fill_lds(pattern, blocks, stream=None):
+    """Every 32-bit word of the LDS of 'blocks' full-LDS workgroups set to
+    'pattern' (tests: LDS a later launch must not read unwritten)."""
+    if lib().cpattn_probe_fill_lds(int(pattern) & 0xFFFFFFFF, int(blocks),
+                                   _stream(stream)) != 0:
+        raise RuntimeError("cpattn_probe_fill_lds failed")

@@ -1,6 +1,7 @@
 // Peak check for the roofline: the bf16 matrix-core rate this part sustains
 // on a stream of v_mfma_f32_32x32x16_bf16 with no memory traffic, the
-// denominator that sits beside the published dense peak.
+// denominator that sits beside the published dense peak.  Also an LDS fill
+// that the memory-safety tests run before each attention launch.
 //
 // Every wave keeps eight independent accumulators and feeds each MFMA a
 // different pair of its eight operand registers (loaded once from the
@@ -57,6 +58,22 @@ mfma_probe(const uint16_t *operands, float *out, int iters) {
     out[(int64_t)blockIdx.x * NT + threadIdx.x] = sum;
 }
 
+// Every 16-byte word of the LDS a workgroup can hold (160 KiB on gfx950) set
+// to one pattern, so one workgroup runs per CU at a time.  The LDS keeps
+// its contents after a kernel ends, so a kernel that ran on a CU before
+// another can leave values the later one might read if it used LDS it had
+// not written.  The asm statement takes the array's address and clobbers
+// memory, so the stores are not removed as dead.
+constexpr int LDS_FILL_WORDS = 160 * 1024 / 16;
+constexpr int LDS_FILL_NT = 256;
+
+__global__ void __launch_bounds__(LDS_FILL_NT) lds_fill(uint32_t pattern) {
+    __shared__ u32x4 words[LDS_FILL_WORDS];
+    const u32x4 v = {pattern, pattern, pattern, pattern};
+    for (int i = threadIdx.x; i < LDS_FILL_WORDS; i += LDS_FILL_NT) words[i] = v;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::"v"((unsigned)(uintptr_t)words) : "memory");
+}
+
 }  // namespace
 }  // namespace cpattn
 
@@ -68,6 +85,13 @@ int cpattn_probe_mfma(const void *operands, float *out, int blocks, int iters, v
     hipLaunchKernelGGL(cpattn::mfma_probe, dim3((unsigned)blocks), dim3(cpattn::NT),
                        cpattn::LDS_RESERVE, (hipStream_t)stream, (const uint16_t *)operands, out,
                        iters);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int cpattn_probe_fill_lds(unsigned pattern, int blocks, void *stream) {
+    if (blocks < 1) return 1;
+    hipLaunchKernelGGL(cpattn::lds_fill, dim3((unsigned)blocks), dim3(cpattn::LDS_FILL_NT), 0,
+                       (hipStream_t)stream, (uint32_t)pattern);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -386,3 +386,5 @@ def test_probe_validation_before_launch():
     assert L.cpattn_probe_mfma(ALIGNED, ALIGNED, 0, 1, None) == 1
     assert L.cpattn_probe_mfma(ALIGNED, ALIGNED, 1, 0, None) == 1
     assert L.cpattn_device_info(None, None) == 1
+    assert L.cpattn_probe_fill_lds(0, 0, None) == 1    # no workgroups
+    assert L.cpattn_probe_fill_lds(0, -4, None) == 1

@@ -150,15 +150,24 @@ def prewarm(torch, fn, seconds=PREWARM_S):
 
 
 def host_cpu_model():
-    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    """The host CPU's model name from /proc/cpuinfo, with its family and
+    model numbers and clock (a virtual machine may report only a vendor
+    name), or None."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break          # the first processor's block is enough
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
     except OSError:
-        pass
-    return None
+        return None
+    name = fields.get("model name")
+    if name is None:
+        return None
+    extra = [f"{k} {fields[k]}" for k in ("cpu family", "model", "cpu MHz") if k in fields]
+    return f"{name} ({', '.join(extra)})" if extra else name
 
 
 def share_fused_tflops(C, torch, P, w, rank, stream, reps=5, warmup=2):

@@ -120,3 +120,11 @@ def test_digest_on_synthetic_profiles(tmp_path):
 def test_digest_needs_its_csv_files(tmp_path):
     with pytest.raises(FileNotFoundError):
         bench.digest(str(tmp_path / "missing"), str(tmp_path))
+
+
+def test_host_cpu_model_names_family_and_model():
+    import bench
+    name = bench.host_cpu_model()
+    if name is None:
+        pytest.skip("no /proc/cpuinfo model name on this host")
+    assert "cpu family" in name and "model" in name, name

@@ -205,3 +205,35 @@ def test_stepwise_calls_equal_forward_entry_point(name, s):
             assert torch.equal(a["steps"][i]["o"], g["steps"][i]["o"]), (r, i)
             assert torch.equal(a["steps"][i]["lse"], g["steps"][i]["lse"]), (r, i)
         assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"]), r
+
+
+def test_resident_steps_grid_full_size_equals_stepwise():
+    """At the 32k headline share (rank 3: 3072 items on one workgroup per
+    CU, each looping over twelve items) the steps' grid writes every step's
+    partial O_i and L_i with the same bits as one launch per step, and
+    cpattn_forward (the grid and the merge) the same merged result."""
+    w = WORKLOADS["bf16_gqa_s32k_cp8"]
+    r = w.rank
+    say(f"resident steps grid vs per-step launches: {w.name} rank {r}, full size")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(21)
+    rnd = lambda *sh: (torch.randn(sh, generator=gen, device="cuda") * 0.5).to(torch.bfloat16)  # noqa
+    q, k, v = rnd(w.b, w.s, w.hq, w.d), rnd(w.b, w.s, w.hkv, w.d), rnd(w.b, w.s, w.hkv, w.d)
+    torch.cuda.synchronize()
+    P = CPProblem(w, q, k, v)          # device inputs are used as they are
+    P.partition()
+    a = P.alloc_rank(r)
+    for i in range(w.cp):
+        P.step(a, i)
+    P.merge(a)
+    g = P.alloc_rank(r)
+    g["ws"].fill_(255)                # NaN pattern: every partial must be written
+    P.steps(g)
+    b = P.alloc_rank(r)
+    P.forward(b)
+    torch.cuda.synchronize()
+    for i in range(w.cp):
+        assert torch.equal(a["steps"][i]["o"], g["steps"][i]["o"]), i
+        assert torch.equal(a["steps"][i]["lse"], g["steps"][i]["lse"]), i
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+    say("  every partial and the merged result equal bit for bit")
